@@ -1,0 +1,240 @@
+/*
+ * zero1.h -- C ABI of libzero1.so: one data-parallel rank's ZeRO-1 optimizer
+ * step on one MI355X (gfx950), in hand-written HIP kernels.
+ *
+ * The step, for rank r of W data-parallel ranks, on r's contiguous shard of
+ * the flat parameter vector (elements [begin, begin+len)):
+ *   1. reduce    g = (sum over w = 0..W-1 of the bf16 gradient of replica w) / W,
+ *                fp32 accumulation in rank order                   (zero1_shard_reduce)
+ *   2. norm      this rank's sum of g^2 (fp64); the global norm is the square
+ *                root of the rank partials added in rank order      (zero1_grad_norm)
+ *   3. clip      if norm > max_norm, g *= max_norm / norm
+ *   4. AdamW     m, v, update, then decoupled decay on the fp32 master
+ *   5. bf16      the forward-pass parameter is the nearest-even bf16 of the
+ *                new master                                          (3-5: zero1_adamw_step)
+ *   1-5 fused over a ragged per-tensor list: zero1_mta_plan + zero1_mta_step.
+ *
+ * Sources (web pages; section names as they appear on each page):
+ *   "并行训练" (notes.cassieliang.com):
+ *       "一张卡上装了什么：混合精度与 AdamW" -- fp32 master, bf16 copy each step,
+ *           AdamW code with the folded bias correction and decay after the update,
+ *           16 B/param (12 B with bf16 m, v);
+ *       "训练循环与 checkpoint" -- global L2-norm clipping of all gradients at max_norm,
+ *           optimizer state (m, v, t) and t restarting at 1;
+ *       "卡和卡怎么说话：集合通信" -- reduce-scatter: rank i receives the sum of block i;
+ *       "数据并行与 ZeRO：按 batch 切，再把状态切碎" -- DDP averages replica gradients;
+ *           ZeRO-1 reduce-scatters the gradients and updates only the own 1/W slice.
+ *   "Stanford CS336 第八讲精读：并行（下）" sec. 五 (four-rank reduce example) and
+ *       sec. 七 (all-reduce with AVG of each gradient).
+ *   "Stanford CS336 第七讲精读：并行（上）" sec. 5.2 (ZeRO stage 1 steps).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer; the library allocates no device memory.  All work is enqueued on
+ *     `stream` (a hipStream_t, NULL = the null stream) and nothing synchronizes:
+ *     results are ready when the stream reaches them, and a fault inside a kernel
+ *     surfaces at the caller's next synchronization.  Setting the environment
+ *     variable ZERO1_SYNC_CHECK=1 makes each call synchronize and check (tests).
+ *   - bf16 values are passed as uint16_t bit patterns; fp32 as float.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call launches nothing and returns an error status, with a
+ *     message from zero1_last_error() (per host thread).
+ *   - len == 0 is a valid no-op.
+ *   - Non-finite values are not errors: they propagate by IEEE rules and
+ *     zero1_norm_info.nonfinite is set when the norm is NaN or infinite.
+ *   - Arithmetic: every fp32 operation is a single IEEE binary32 operation
+ *     rounded to nearest-even (no fused multiply-add, correctly rounded divide
+ *     and square root, subnormals kept); sums of squares are fp64; scalars
+ *     derived from the hyper-parameters are formed in fp64 on the host and
+ *     rounded once to fp32.
+ *   - Calls that share a workspace must not overlap in time (same stream, or
+ *     ordered by the caller).
+ */
+#ifndef ZERO1_H
+#define ZERO1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO1_ABI_VERSION 1
+#define ZERO1_MAX_W 128          /* largest number of replicas per call */
+
+typedef enum zero1_status {
+    ZERO1_OK = 0,
+    ZERO1_EINVAL = 1,            /* bad argument (message says which)            */
+    ZERO1_EWORKSPACE = 2,        /* workspace NULL, too small or misaligned       */
+    ZERO1_EHIP = 3,              /* a HIP runtime call failed (message has it)    */
+    ZERO1_ENOTSUPPORTED = 4      /* current device is not gfx950                  */
+} zero1_status;
+
+/* flags (bitwise OR) */
+#define ZERO1_SUM_ONLY     0x1u  /* reduce: keep the sum, do not divide by W        */
+#define ZERO1_MV_BF16      0x2u  /* m and v are stored as bf16 (uint16_t)           */
+#define ZERO1_RECOMPUTE_G  0x4u  /* step: the update re-reads the W slices          */
+#define ZERO1_STORE_G      0x8u  /* step: the reduce stores fp32 g in the workspace
+                                    and the update reads it back.  Neither flag:
+                                    the library picks the design with fewer bytes
+                                    (STORE_G when W > 4).                            */
+
+/* AdamW and clipping hyper-parameters of one step (host struct). */
+typedef struct zero1_hparams {
+    double lr;              /* >= 0                                             */
+    double beta1;           /* in [0, 1)                                        */
+    double beta2;           /* in [0, 1)                                        */
+    double eps;             /* >= 0                                             */
+    double weight_decay;    /* >= 0; decay factor 1 - lr*weight_decay           */
+    double max_norm;        /* > 0; +inf disables clipping                      */
+    int64_t step;           /* t >= 1 (bias correction uses beta^t)             */
+} zero1_hparams;
+
+/* Result of the clip stage, written to device memory by the step calls. */
+typedef struct zero1_norm_info {
+    double sumsq_total;     /* sum over ranks of the partial sums of squares    */
+    double norm;            /* sqrt(sumsq_total), fp64                          */
+    float clip_coef;        /* fp32(max_norm / norm) when clip, else 1          */
+    int32_t clip;           /* 1 when norm > max_norm                           */
+    int32_t nonfinite;      /* 1 when norm is NaN or infinite                   */
+    int32_t reserved;
+} zero1_norm_info;
+
+/* One tensor's part of this rank's shard (multi-tensor front end).
+ * Elements [shard_offset, shard_offset + numel) of the shard belong to it;
+ * its state and bf16 parameter are stored at the four pointers. */
+typedef struct zero1_piece {
+    int64_t numel;          /* > 0                                              */
+    int64_t shard_offset;   /* position of its first element inside the shard   */
+    uint16_t* param_bf16;   /* numel bf16, written                              */
+    float* master;          /* numel fp32, read and written                     */
+    void* m;                /* numel fp32 (bf16 with ZERO1_MV_BF16), r/w        */
+    void* v;                /* numel fp32 (bf16 with ZERO1_MV_BF16), r/w        */
+} zero1_piece;
+
+/* A validated piece list uploaded into device memory by zero1_mta_plan.
+ * Plain data owned by the caller; valid as long as the table memory is. */
+typedef struct zero1_plan {
+    void* table;            /* device: piece descriptors + chunk table          */
+    int64_t shard_len;      /* sum of the pieces' numel                          */
+    int32_t n_pieces;
+    int32_t n_chunks;
+    int32_t chunk_elems;    /* elements per chunk (pieces are cut into chunks)  */
+    uint32_t flags;         /* ZERO1_MV_BF16 as given to zero1_mta_plan          */
+    int32_t aligned;        /* 1 when every piece allows 16-byte vector access  */
+    int32_t reserved;
+} zero1_plan;
+
+/* ---------------------------------------------------------------- misc */
+int zero1_abi_version(void);
+/* Message of the last failing call on this host thread ("" if none). */
+const char* zero1_last_error(void);
+const char* zero1_status_string(int status);
+
+/* Host-only: rank's shard of an n_total-element flat vector cut into W
+ * contiguous shards of S = ceil(n_total / W) elements (the last may be
+ * short or empty): *begin = min(rank*S, n_total), *len = its length.
+ * Rank i holding block i is the reduce-scatter convention of "并行训练",
+ * section "卡和卡怎么说话：集合通信". */
+zero1_status zero1_shard_range(int64_t n_total, int W, int rank,
+                               int64_t* begin, int64_t* len);
+
+/* Bytes of workspace needed by the flat entry points for a shard of `len`
+ * elements (flags as passed to the call: ZERO1_STORE_G adds 4*len). */
+size_t zero1_workspace_bytes(int64_t len, int W, uint32_t flags);
+
+/* ---------------------------------------------------------------- step 1 (+2)
+ * Reduce-scatter arithmetic on one rank's shard.
+ * ("卡和卡怎么说话：集合通信" reduce-scatter; "Stanford CS336 第八讲精读" sec. 七 AVG.)
+ *   grads     (host) array of W device pointers; grads[w] is replica w's flat
+ *             gradient (bf16), indexed by flat position.
+ *   W         1..ZERO1_MAX_W replicas.
+ *   begin,len the shard [begin, begin+len) of the flat vector.
+ *   flags     ZERO1_SUM_ONLY: output the sum instead of the average.
+ *   g_out     len fp32 outputs g[k] for flat element begin+k, or NULL.
+ *             Must not overlap any gradient range.
+ *   sumsq_out one double: sum of g[k]^2 over the shard (fp64, fixed order,
+ *             deterministic), or NULL.  At least one of g_out, sumsq_out.
+ *   ws        workspace of zero1_workspace_bytes(len, W, 0) bytes, 256-byte
+ *             aligned (needed only when sumsq_out != NULL).
+ * Accumulation: s = widen(G_0); s = s + widen(G_w) for w = 1..W-1; g = s / W. */
+zero1_status zero1_shard_reduce(const uint16_t* const* grads, int W,
+                                int64_t begin, int64_t len, uint32_t flags,
+                                float* g_out, double* sumsq_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- step 2
+ * This rank's partial of the global L2 norm ("训练循环与 checkpoint": the norm of
+ * all gradients taken as one vector): *sumsq_out = sum of g[k]^2, k < len,
+ * squares exact in fp64, fp64 adds in a fixed order (deterministic).
+ *   g         len fp32 values.   ws: zero1_workspace_bytes(len, 1, 0) bytes. */
+zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- steps 3-5
+ * Clip and AdamW on a flat shard, then the bf16 copy
+ * ("一张卡上装了什么：混合精度与 AdamW"; clip from "训练循环与 checkpoint").
+ *   g           len fp32 reduced gradients, or NULL to recompute them from
+ *               grads/W/begin (same arithmetic as zero1_shard_reduce).
+ *   grads,W,begin  as for zero1_shard_reduce; ignored when g != NULL.
+ *   master      len fp32, updated in place.
+ *   m, v        len fp32 (or bf16 with ZERO1_MV_BF16), updated in place;
+ *               zero before the first step.
+ *   param_bf16  len bf16 outputs: nearest-even bf16 of the new master.
+ *   hp          (host) hyper-parameters; hp->step is t.
+ *   rank_sumsq  n_ranks doubles: every rank's partial sum of squares (this
+ *               rank's included), added in rank order for the global norm.
+ *   flags       ZERO1_MV_BF16, ZERO1_SUM_ONLY (with g == NULL).
+ *   info_out    one zero1_norm_info (device) or NULL.
+ *   ws          zero1_workspace_bytes(len, W, 0) bytes.
+ * Per element, with c the clip coefficient when clipping:
+ *   g' = g*c;  m = b1*m + a1*g';  v = b2*v + a2*(g'*g');
+ *   p = p - sigma*(m / (sqrt(v) + eps));  p = p*delta;  param = bf16(p)
+ * where b1 = fp32(beta1), a1 = fp32(1-beta1), b2, a2 likewise, eps = fp32(eps),
+ * sigma = fp32(lr*sqrt(1-beta2^t)/(1-beta1^t)), delta = fp32(1-lr*weight_decay).
+ * The state buffers and param_bf16 must not overlap each other or g. */
+zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads,
+                              int W, int64_t begin, int64_t len,
+                              float* master, void* m, void* v,
+                              uint16_t* param_bf16, const zero1_hparams* hp,
+                              const double* rank_sumsq, int n_ranks,
+                              uint32_t flags, zero1_norm_info* info_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- fused step
+ * Multi-tensor apply over a ragged per-tensor list (the parameter list the
+ * training loop hands to clipping and the optimizer, "训练循环与 checkpoint").
+ *
+ * zero1_mta_table_bytes: device bytes the plan table needs for this list.
+ * zero1_mta_plan: validates the pieces (numel > 0; together they tile
+ *   [0, shard_len) exactly, in any order; no two buffers overlap), cuts them
+ *   into chunks and copies the table into `table` (device, 256-byte aligned,
+ *   table_bytes long).  Synchronous: call once per tensor-list layout and
+ *   reuse the plan for every step.  `flags` may hold ZERO1_MV_BF16.
+ * zero1_mta_workspace_bytes: step workspace for this plan and W.
+ * zero1_mta_step: the whole step (1-5) for rank my_rank:
+ *   grads, W, begin  as for zero1_shard_reduce (the shard's gradient slices).
+ *   rank_sumsq  n_ranks doubles: the other ranks' partials on entry; entry
+ *               my_rank is overwritten with this rank's partial before the
+ *               norm is formed (the partials of the other ranks are the only
+ *               value a multi-GPU run would have to exchange mid-step).
+ *   flags       ZERO1_STORE_G / ZERO1_RECOMPUTE_G / ZERO1_SUM_ONLY
+ *               (ZERO1_MV_BF16 comes from the plan).
+ *   Results are bit-identical to zero1_shard_reduce + zero1_adamw_step. */
+size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces);
+zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces,
+                            uint32_t flags, void* table, size_t table_bytes,
+                            zero1_plan* plan_out);
+size_t zero1_mta_workspace_bytes(const zero1_plan* plan, int W, uint32_t flags);
+zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
+                            const zero1_plan* plan, const zero1_hparams* hp,
+                            double* rank_sumsq, int n_ranks, int my_rank,
+                            uint32_t flags, zero1_norm_info* info_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO1_H */

@@ -1,0 +1,405 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element, on seeded inputs that span several tiles, ragged tails, misaligned
+starts, special values and every rank.  Floating-point results must be
+bit-identical to the oracle (the operation sequence is the same); norms, whose
+fp64 partial sums are added in a different order, must agree to 1e-12
+relative, and the clip decision and coefficient must be identical."""
+from __future__ import annotations
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import zero_sharded_mixed_zero1_amd as z
+from synth.workloads import shard_range
+from tests.gpu_util import (MtaShard, assert_bf16_equal, assert_f32_equal, rel_close, to_dev_u16,
+                            to_np_u16, torch_cuda, ws_tensor)
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL = 1e-12
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    return torch, dev
+
+
+def hp_at(t, **kw):
+    d = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0, step=t)
+    d.update(kw)
+    return d
+
+
+SPECIALS = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x4000,
+                     0x3C00, 0x7F7F, 0x00FF], dtype=np.uint16)
+
+
+def replicas(seed, t, W, N, sigma, outlier_pct=0, specials=0, rng=None):
+    G = [synth.bf16(N, synth.grad_key(seed, t, w), 0, sigma, outlier_pct) for w in range(W)]
+    if specials and N:
+        rng = rng or np.random.default_rng(seed + t)
+        for g in G:
+            idx = rng.choice(N, size=min(specials, N), replace=False)
+            g[idx] = rng.choice(SPECIALS, size=idx.size)
+    return G
+
+
+# ---------------------------------------------------------------- input generator
+def test_synth_gpu_matches_cpu(env):
+    torch, dev = env
+    for n, i0, sigma, pct in [(1, 0, 1e-3, 0), (1000003, 17, 1e-2, 1), (4096, 1 << 40, 0.02, 0),
+                              (333333, 5_000_000_000, 1e-3, 7)]:
+        k = synth.grad_key(0xABCDEF, 3, 5)
+        tb = torch.empty(n, dtype=torch.int16, device=dev)
+        synth.fill_bf16_(tb, k, i0, sigma, pct)
+        tf = torch.empty(n, dtype=torch.float32, device=dev)
+        synth.fill_f32_(tf, k, i0, sigma, pct)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np_u16(tb), synth.bf16(n, k, i0, sigma, pct))
+        assert np.array_equal(tf.cpu().numpy().view(np.uint32), synth.f32(n, k, i0, sigma, pct).view(np.uint32))
+
+
+# ---------------------------------------------------------------- reduce + norm
+LENGTHS = [0, 1, 7, 8, 9, 2047, 2048, 2049, 16384 + 5, 3 * 65536 + 13]
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 64])
+def test_shard_reduce_parity(env, W):
+    torch, dev = env
+    ws = ws_tensor(torch, z.workspace_bytes(1 << 20, W), dev)
+    sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    for length in LENGTHS:
+        for offset in (0, 1, 3, 8):
+            if W == 64 and offset not in (0, 3):
+                continue
+            N = offset + length + 5
+            G = replicas(1000 + W, length + offset, W, N, 0.5, outlier_pct=2, specials=3)
+            gd = [to_dev_u16(torch, g, dev) for g in G]
+            for flags in (0, z.SUM_ONLY):
+                gout = torch.full((length + 4,), float("nan"), dtype=torch.float32, device=dev)
+                go = gout[1:] if offset == 3 else gout       # also a misaligned output
+                z.shard_reduce(gd, offset, length, g_out=go, sumsq_out=sumsq, flags=flags, ws=ws)
+                torch.cuda.synchronize()
+                exp = oracle.shard_reduce([g[offset:offset + length] for g in G],
+                                          average=not (flags & z.SUM_ONLY))
+                got = go[:length].cpu().numpy()
+                assert_f32_equal(got, exp, f"g W={W} len={length} off={offset} flags={flags}")
+                assert np.isnan(go[length:].cpu().numpy()).all(), "wrote past the end"
+                q = float(sumsq.item())
+                assert rel_close(q, oracle.sumsq(exp), NORM_TOL), (W, length, offset, q)
+            # norm only (no g_out) gives the same partial bit for bit
+            s2 = torch.zeros(1, dtype=torch.float64, device=dev)
+            z.shard_reduce(gd, offset, length, sumsq_out=s2, ws=ws)
+            z.shard_reduce(gd, offset, length, g_out=gout, sumsq_out=sumsq, ws=ws)
+            torch.cuda.synchronize()
+            assert s2.item() == sumsq.item()
+
+
+def test_grad_norm_parity(env):
+    torch, dev = env
+    ws = ws_tensor(torch, z.workspace_bytes(1 << 22, 1), dev)
+    out = torch.zeros(1, dtype=torch.float64, device=dev)
+    for n in (0, 1, 9, 2048, 65536 * 5 + 3, 3_000_001):
+        x = synth.f32(n + 1, synth.key(77, n), 0, 3.0, 1)
+        x[:: max(1, n // 7)] = np.float32(1e-42)     # subnormals
+        t = torch.from_numpy(x).to(dev)
+        for view in (t[:n], t[1:n + 1]):
+            z.grad_norm(view, n, out, ws=ws)
+            torch.cuda.synchronize()
+            exp = oracle.sumsq(view.cpu().numpy())
+            assert rel_close(out.item(), exp, NORM_TOL), (n, out.item(), exp)
+    # the fp32 g of shard_reduce and its partial agree with grad_norm over that g
+    G = replicas(5, 1, 3, 100_000, 1e-2)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    g = torch.empty(100_000, dtype=torch.float32, device=dev)
+    s1 = torch.zeros(1, dtype=torch.float64, device=dev)
+    z.shard_reduce(gd, 0, 100_000, g_out=g, sumsq_out=s1, ws=ws)
+    z.grad_norm(g, 100_000, out, ws=ws)
+    torch.cuda.synchronize()
+    assert s1.item() == out.item()
+
+
+# ---------------------------------------------------------------- flat AdamW
+@pytest.mark.parametrize("mv_bf16", [False, True])
+@pytest.mark.parametrize("source", ["g", "recompute3", "recompute8"])
+def test_adamw_step_flat_parity(env, mv_bf16, source):
+    torch, dev = env
+    W = {"g": 4, "recompute3": 3, "recompute8": 8}[source]
+    for length, offset, max_norm, t0 in [(1, 0, 1.0, 1), (2049, 0, 1.0, 1), (65536 * 3 + 7, 0, 1e9, 2),
+                                         (4103, 5, 1.0, 999), (20000, 8, math.inf, 1)]:
+        seed = zlib.crc32(f"{length}/{offset}/{source}".encode()) & 0xFFFFFF
+        N = offset + length
+        master0 = synth.f32(N, synth.master_key(seed), 0, 0.02)[offset:]
+        k = min(3, length)
+        master0[:k] = np.array([1e-40, -0.0, 3e38], dtype=np.float32)[:k]
+        mvd = torch.int16 if mv_bf16 else torch.float32
+        npmv = np.uint16 if mv_bf16 else np.float32
+        gm = torch.from_numpy(master0.copy()).to(dev)
+        gmm = torch.zeros(length, dtype=mvd, device=dev)
+        gvv = torch.zeros(length, dtype=mvd, device=dev)
+        gp = torch.zeros(length + 1, dtype=torch.int16, device=dev)[1:] if offset == 5 else \
+            torch.zeros(length, dtype=torch.int16, device=dev)
+        om, ov = np.zeros(length, npmv), np.zeros(length, npmv)
+        omaster, oparam = master0.copy(), np.zeros(length, np.uint16)
+        ws = ws_tensor(torch, z.workspace_bytes(length, W), dev)
+        info = torch.zeros(4, dtype=torch.float64, device=dev)
+        gbuf = torch.empty(length, dtype=torch.float32, device=dev)
+        for t in range(t0, t0 + 3):
+            G = replicas(seed, t, W, N, 0.05 if t % 2 else 0.001, outlier_pct=1, specials=2)
+            sl = [g[offset:] for g in G]
+            hp = hp_at(t, max_norm=max_norm)
+            other = np.array([0.0, 0.37, 0.0], dtype=np.float64)     # three "ranks"; we are rank 0
+            rs = other.copy()
+            oinfo = oracle.step(sl, omaster, om, ov, oparam, hp, rs, 0)
+            gd = [to_dev_u16(torch, g, dev) for g in G]
+            rsd = torch.from_numpy(rs).to(dev)                      # includes this rank's oracle partial
+            if source == "g":
+                sq = torch.zeros(1, dtype=torch.float64, device=dev)
+                z.shard_reduce(gd, offset, length, g_out=gbuf, sumsq_out=sq, ws=ws)
+                torch.cuda.synchronize()
+                assert rel_close(sq.item(), rs[0], NORM_TOL)
+                z.adamw_step(gbuf, None, 0, length, gm, gmm, gvv, gp, hp, rsd, 3,
+                             flags=z.MV_BF16 if mv_bf16 else 0, info_out=info, ws=ws)
+            else:
+                z.adamw_step(None, gd, offset, length, gm, gmm, gvv, gp, hp, rsd, 3,
+                             flags=z.MV_BF16 if mv_bf16 else 0, info_out=info, ws=ws)
+            torch.cuda.synchronize()
+            ni = info.cpu().numpy()
+            assert ni[1] == oinfo.norm                        # same partials in, same norm out
+            iw = info.cpu().numpy().view(np.int32)
+            assert bool(iw[5]) == oinfo.clip
+            assert info.cpu().numpy()[2:3].view(np.float32)[0] == oinfo.coef
+        what = f"len={length} off={offset} src={source} bf16mv={mv_bf16}"
+        assert_f32_equal(gm.cpu().numpy(), omaster, "master " + what)
+        if mv_bf16:
+            assert_bf16_equal(to_np_u16(gmm), om, "m " + what)
+            assert_bf16_equal(to_np_u16(gvv), ov, "v " + what)
+        else:
+            assert_f32_equal(gmm.cpu().numpy(), om, "m " + what)
+            assert_f32_equal(gvv.cpu().numpy(), ov, "v " + what)
+        assert_bf16_equal(to_np_u16(gp), oparam, "param " + what)
+
+
+# ---------------------------------------------------------------- multi-tensor apply
+RAGGED = [3000, 17, 5000, 8, 2203, 1, 65536 + 3, 768, 8192 * 2, 40000]
+
+
+def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_state, sigma_fn,
+                      max_norm=1.0, ranks=None):
+    N = sum(numels)
+    ranks = list(range(W)) if ranks is None else ranks
+    master_full = synth.f32(N, synth.master_key(seed), 0, 0.02)
+    shards = {r: MtaShard(torch, dev, numels, W, r, master_full, mv_bf16, flat_state) for r in ranks}
+    wss = {r: shards[r].workspace(flags) for r in ranks}
+    from tests.oracle_sim import RankState
+    ost = {r: RankState(master_full[slice(*shard_range(N, W, r))], mv_bf16) for r in ranks}
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    ws_r = ws_tensor(torch, z.workspace_bytes(N, W), dev)
+    infos = torch.zeros((W, 4), dtype=torch.float64, device=dev)
+    for t in range(1, steps + 1):
+        G = replicas(seed, t, W, N, sigma_fn(t), outlier_pct=1)
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        part = np.zeros(W)
+        for r in range(W):
+            b, e = shard_range(N, W, r)
+            part[r] = oracle.sumsq(oracle.shard_reduce([g[b:e] for g in G]))
+            # every rank's partial from the GPU (what the mid-step exchange would deliver)
+            z.shard_reduce(gd, b, e - b, sumsq_out=rsd[r:r + 1], ws=ws_r)
+        torch.cuda.synchronize()
+        gpu_part = rsd.cpu().numpy().copy()
+        for r in range(W):
+            assert rel_close(gpu_part[r], part[r], NORM_TOL)
+        hp = hp_at(t, max_norm=max_norm)
+        for r in ranks:
+            b, e = shard_range(N, W, r)
+            rs = part.copy()
+            oi = oracle.step([g[b:e] for g in G], ost[r].master, ost[r].m, ost[r].v, ost[r].param, hp, rs, r)
+            rsd.copy_(torch.from_numpy(gpu_part))
+            z.mta_step(gd, b, shards[r].plan, hp, rsd, W, r, flags=flags, info_out=infos[r], ws=wss[r])
+            torch.cuda.synchronize()
+            ni = infos[r].cpu().numpy()
+            assert rel_close(ni[1], oi.norm, NORM_TOL)
+            assert bool(ni[2:4].view(np.int32)[1]) == oi.clip
+            assert ni[2:3].view(np.float32)[0] == oi.coef
+            assert rel_close(rsd[r].item(), part[r], NORM_TOL)
+    for r in ranks:
+        master, m, v, param = shards[r].gather()
+        what = f"rank {r}/{W} flags={flags} bf16mv={mv_bf16} flat={flat_state}"
+        assert_f32_equal(master, ost[r].master, "master " + what)
+        if mv_bf16:
+            assert_bf16_equal(m, ost[r].m, "m " + what)
+            assert_bf16_equal(v, ost[r].v, "v " + what)
+        else:
+            assert_f32_equal(m, ost[r].m, "m " + what)
+            assert_f32_equal(v, ost[r].v, "v " + what)
+        assert_bf16_equal(param, ost[r].param, "param " + what)
+        assert shards[r].untouched_outside(), "wrote outside the shard's pieces: " + what
+    return shards, ost
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
+def test_mta_parity_ragged_all_ranks(env, W, design):
+    torch, dev = env
+    run_mta_all_ranks(torch, dev, RAGGED, W, 3, 0xA000 + W, design, False, True,
+                      lambda t: [0.02, 1e-4, 0.3][t % 3])
+
+
+@pytest.mark.parametrize("mv_bf16,flat_state", [(True, True), (False, False), (True, False)])
+def test_mta_parity_state_layouts(env, mv_bf16, flat_state):
+    torch, dev = env
+    for design in (z.STORE_G, z.RECOMPUTE_G):
+        run_mta_all_ranks(torch, dev, RAGGED, 4, 3, 0xB000, design, mv_bf16, flat_state,
+                          lambda t: [0.02, 1e-4, 0.3][t % 3])
+
+
+def test_mta_misaligned_pieces(env):
+    """Pieces whose lengths are not multiples of 8 make later pieces start off
+    the 16-byte grid: the library must take its element-wise path and still
+    match the oracle."""
+    torch, dev = env
+    run_mta_all_ranks(torch, dev, [13, 1001, 7, 4099, 65536 + 1], 3, 3, 0xC000, 0, False, False,
+                      lambda t: 0.1)
+
+
+def test_c1_full_trajectory(env):
+    """C1: flat 2^20 parameters, W=4, every rank, 10 steps, against the oracle."""
+    from synth.workloads import configs
+    c = configs()["C1"]
+    torch, dev = env
+    run_mta_all_ranks(torch, dev, [c.n_total], c.W, c.steps, c.seed, 0, False, True,
+                      lambda t: c.sigma)
+
+
+# ---------------------------------------------------------------- properties
+def test_mta_equals_reduce_plus_adamw(env):
+    torch, dev = env
+    W, numels = 8, [50000, 3, 70001]
+    N = sum(numels)
+    r = 5
+    master_full = synth.f32(N, synth.master_key(9), 0, 0.02)
+    a = MtaShard(torch, dev, numels, W, r, master_full)
+    b0, S = a.begin, a.S
+    fm = torch.from_numpy(master_full[b0:b0 + S].copy()).to(dev)
+    fmm = torch.zeros(S, dtype=torch.float32, device=dev)
+    fvv = torch.zeros(S, dtype=torch.float32, device=dev)
+    fp = torch.zeros(S, dtype=torch.int16, device=dev)
+    ws1, ws2 = a.workspace(z.STORE_G), ws_tensor(torch, z.workspace_bytes(S, W), dev)
+    g = torch.empty(S, dtype=torch.float32, device=dev)
+    for t in range(1, 4):
+        G = replicas(9, t, W, N, 0.3)
+        gd = [to_dev_u16(torch, x, dev) for x in G]
+        rs1 = torch.full((W,), 0.125, dtype=torch.float64, device=dev)
+        rs2 = rs1.clone()
+        z.mta_step(gd, b0, a.plan, hp_at(t), rs1, W, r, flags=z.STORE_G, ws=ws1)
+        z.shard_reduce(gd, b0, S, g_out=g, sumsq_out=rs2[r:r + 1], ws=ws2)
+        z.adamw_step(g, None, 0, S, fm, fmm, fvv, fp, hp_at(t), rs2, W, ws=ws2)
+        torch.cuda.synchronize()
+        assert rs1[r].item() == rs2[r].item()
+    master, m, v, param = a.gather()
+    assert_f32_equal(master, fm.cpu().numpy(), "master")
+    assert_f32_equal(m, fmm.cpu().numpy(), "m")
+    assert_f32_equal(v, fvv.cpu().numpy(), "v")
+    assert_bf16_equal(param, to_np_u16(fp), "param")
+
+
+def test_rerun_is_bit_identical_and_resume_is_exact(env):
+    torch, dev = env
+    W, numels, r = 4, [100_000, 33_333, 7], 2
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(11), 0, 0.02)
+    runs = []
+    for mode in ("straight", "straight", "resume"):
+        a = MtaShard(torch, dev, numels, W, r, master_full)
+        ws = a.workspace()
+        norms = []
+        for t in range(1, 7):
+            if mode == "resume" and t == 4:
+                # checkpoint m, v, master (t is an argument), then restore into fresh buffers
+                saved = [tuple(x.clone().cpu() for x in s) for s in a.state]
+                a = MtaShard(torch, dev, numels, W, r, master_full)
+                ws = a.workspace()
+                for dst, src in zip(a.state, saved):
+                    for d, s in zip(dst, src):
+                        d.copy_(s.to(dev))
+            G = replicas(11, t, W, N, 0.2)
+            gd = [to_dev_u16(torch, x, dev) for x in G]
+            rs = torch.full((W,), 0.5, dtype=torch.float64, device=dev)
+            info = torch.zeros(4, dtype=torch.float64, device=dev)
+            z.mta_step(gd, a.begin, a.plan, hp_at(t), rs, W, r, info_out=info, ws=ws)
+            torch.cuda.synchronize()
+            norms.append(info.cpu().numpy().tobytes())
+        runs.append((a.gather(), norms))
+    (s0, n0), (s1, n1), (s2, n2) = runs
+    assert n0 == n1 == n2
+    for x, y, q in zip(s0, s1, s2):
+        assert x.tobytes() == y.tobytes() == q.tobytes()
+
+
+def test_nonfinite_gradient_propagates(env):
+    torch, dev = env
+    W, N = 3, 30000
+    G = replicas(21, 1, W, N, 0.01)
+    G[1][12345] = 0x7FC0          # NaN in one replica
+    G[2][777] = 0x7F80            # +inf in another
+    master0 = synth.f32(N, synth.master_key(21), 0, 0.02)
+    for max_norm in (1.0, math.inf):
+        om, ov = np.zeros(N, np.float32), np.zeros(N, np.float32)
+        omaster, oparam = master0.copy(), np.zeros(N, np.uint16)
+        rs = np.zeros(1)
+        oi = oracle.step(G, omaster, om, ov, oparam, hp_at(1, max_norm=max_norm), rs, 0)
+        gd = [to_dev_u16(torch, x, dev) for x in G]
+        gm = torch.from_numpy(master0.copy()).to(dev)
+        gmm = torch.zeros(N, dtype=torch.float32, device=dev)
+        gvv = torch.zeros(N, dtype=torch.float32, device=dev)
+        gp = torch.zeros(N, dtype=torch.int16, device=dev)
+        ws = ws_tensor(torch, z.workspace_bytes(N, W), dev)
+        rsd = torch.zeros(1, dtype=torch.float64, device=dev)
+        info = torch.zeros(4, dtype=torch.float64, device=dev)
+        z.shard_reduce(gd, 0, N, sumsq_out=rsd, ws=ws)
+        z.adamw_step(None, gd, 0, N, gm, gmm, gvv, gp, hp_at(1, max_norm=max_norm), rsd, 1,
+                     info_out=info, ws=ws)
+        torch.cuda.synchronize()
+        ni = info.cpu().numpy()
+        assert np.isnan(ni[1]) and np.isnan(oi.norm)
+        assert ni[2:4].view(np.int32)[1] == 0 and not oi.clip      # NaN norm: no clip
+        assert info.cpu().numpy()[3:4].view(np.int32)[0] == 1       # nonfinite flag
+        assert_f32_equal(gm.cpu().numpy(), omaster, "master with NaN/inf")
+        assert_bf16_equal(to_np_u16(gp), oparam, "param with NaN/inf")
+
+
+def test_bf16_stagnation_on_gpu(env):
+    """A constant +2^-10 gradient, lr=1e-3, no decay, no clip, 1000 steps from
+    master 1.0: the fp32 master walks to ~0 exactly as the oracle does, and the
+    bf16 parameter follows it instead of sticking at 1.0."""
+    torch, dev = env
+    n = 64
+    g = np.full(n, 0x3A80, dtype=np.uint16)          # 2^-10 in bf16
+    gd = [to_dev_u16(torch, g, dev)]
+    gm = torch.ones(n, dtype=torch.float32, device=dev)
+    gmm = torch.zeros(n, dtype=torch.float32, device=dev)
+    gvv = torch.zeros(n, dtype=torch.float32, device=dev)
+    gp = torch.zeros(n, dtype=torch.int16, device=dev)
+    ws = ws_tensor(torch, z.workspace_bytes(n, 1), dev)
+    rsd = torch.zeros(1, dtype=torch.float64, device=dev)
+    om, ov = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    omaster, oparam = np.ones(n, np.float32), np.zeros(n, np.uint16)
+    for t in range(1, 1001):
+        hp = hp_at(t, weight_decay=0.0, max_norm=math.inf)
+        z.shard_reduce(gd, 0, n, sumsq_out=rsd, ws=ws)
+        z.adamw_step(None, gd, 0, n, gm, gmm, gvv, gp, hp, rsd, 1, ws=ws)
+        oracle.step([g], omaster, om, ov, oparam, hp, np.zeros(1), 0)
+    torch.cuda.synchronize()
+    assert_f32_equal(gm.cpu().numpy(), omaster, "master after 1000 steps")
+    assert abs(float(omaster[0])) < 2e-3
+    p = to_np_u16(gp)
+    assert_bf16_equal(p, oparam, "param after 1000 steps")
+    assert np.all(oracle.bf16_to_f32(p) < 2e-3)

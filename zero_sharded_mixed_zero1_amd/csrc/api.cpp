@@ -1,0 +1,503 @@
+// api.cpp -- C ABI of libzero1.so (declared in include/zero1.h): argument
+// validation, fp64 derivation of the per-step fp32 scalars, workspace layout,
+// the multi-tensor plan builder, and the launch sequence of each entry point.
+// No entry point allocates device memory or synchronizes (except
+// zero1_mta_plan, which copies its table once, and ZERO1_SYNC_CHECK=1).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/zero1.h"
+#include "internal.h"
+
+using namespace z1;
+
+static_assert(sizeof(NormInfo) == sizeof(zero1_norm_info), "norm info layout");
+static_assert(sizeof(PieceDesc) == 48 && sizeof(ChunkDesc) == 16, "descriptor layout");
+static_assert(kMaxW == ZERO1_MAX_W, "max W");
+
+namespace {
+
+// ------------------------------------------------------------------ errors
+thread_local std::string g_last_error;
+
+zero1_status fail(zero1_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+zero1_status ok()
+{
+    g_last_error.clear();
+    return ZERO1_OK;
+}
+
+#define Z1_HIP(call)                                                                       \
+    do {                                                                                   \
+        hipError_t e_ = (call);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail(ZERO1_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));       \
+    } while (0)
+
+bool sync_check_enabled()
+{
+    static const bool on = [] {
+        const char* s = std::getenv("ZERO1_SYNC_CHECK");
+        return s && s[0] && s[0] != '0';
+    }();
+    return on;
+}
+
+zero1_status finish(hipStream_t s)
+{
+    if (sync_check_enabled()) {
+        Z1_HIP(hipStreamSynchronize(s));
+        Z1_HIP(hipGetLastError());
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------ device
+struct DevInfo {
+    bool probed = false;
+    bool gfx950 = false;
+    int cus = 0;
+    char arch[64] = {0};
+};
+
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+zero1_status current_device(DevInfo& out)
+{
+    int dev = 0;
+    Z1_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(ZERO1_ENOTSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DevInfo& d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t p;
+        Z1_HIP(hipGetDeviceProperties(&p, dev));
+        std::snprintf(d.arch, sizeof d.arch, "%s", p.gcnArchName);
+        d.gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        d.cus = p.multiProcessorCount;
+        d.probed = true;
+    }
+    if (!d.gfx950) return fail(ZERO1_ENOTSUPPORTED, "device %d is %s; libzero1 is built for gfx950", dev, d.arch);
+    out = d;
+    return ZERO1_OK;
+}
+
+// ------------------------------------------------------------------ layout
+constexpr size_t kInfoBytes = 256;
+constexpr size_t kPartialBytes = sizeof(double) * kMaxPartials;
+constexpr size_t kGOffset = kInfoBytes + kPartialBytes;   // multiple of 256
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Ws {
+    NormInfo* info;
+    double* partials;
+    float* g;   // nullptr unless the design stores g
+};
+
+zero1_status carve(void* ws, size_t bytes, size_t need, bool want_g, Ws& out)
+{
+    if (!ws) return fail(ZERO1_EWORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(ZERO1_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (bytes < need) return fail(ZERO1_EWORKSPACE, "workspace has %zu bytes, needs %zu", bytes, need);
+    char* b = static_cast<char*>(ws);
+    out.info = reinterpret_cast<NormInfo*>(b);
+    out.partials = reinterpret_cast<double*>(b + kInfoBytes);
+    out.g = want_g ? reinterpret_cast<float*>(b + kGOffset) : nullptr;
+    return ZERO1_OK;
+}
+
+// Workgroups for a grid-stride pass over `units` tiles: enough to fill every
+// CU several times over, never more than there are tiles.
+int grid_for(int64_t units, const DevInfo& d, int per_cu)
+{
+    int64_t cap = (int64_t)d.cus * per_cu;
+    if (cap > kMaxPartials) cap = kMaxPartials;
+    int64_t n = units < cap ? units : cap;
+    return (int)(n > 0 ? n : 1);
+}
+
+int64_t tiles(int64_t len, bool vec) { return (len + (int64_t)kThreads * (vec ? kVec : 1) - 1) / ((int64_t)kThreads * (vec ? kVec : 1)); }
+
+constexpr int kReducePerCu = 8;
+constexpr int kAdamPerCu = 8;
+
+// ------------------------------------------------------------------ checks
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+zero1_status check_grads(const uint16_t* const* grads, int W, int64_t begin, int64_t len, Reduce& r,
+                         bool sum_only, bool& vec_ok)
+{
+    if (W < 1 || W > kMaxW) return fail(ZERO1_EINVAL, "W=%d must be in [1, %d]", W, kMaxW);
+    if (len < 0) return fail(ZERO1_EINVAL, "len=%lld is negative", (long long)len);
+    if (begin < 0) return fail(ZERO1_EINVAL, "begin=%lld is negative", (long long)begin);
+    if (!grads) return fail(ZERO1_EINVAL, "grads (host array of W pointers) is NULL");
+    vec_ok = true;
+    std::memset(&r, 0, sizeof r);
+    for (int w = 0; w < W; ++w) {
+        if (!grads[w]) return fail(ZERO1_EINVAL, "grads[%d] is NULL", w);
+        r.gp.p[w] = grads[w] + begin;
+        if (!aligned16(r.gp.p[w])) vec_ok = false;
+    }
+    r.W = W;
+    if (sum_only || W == 1) {
+        r.mode = kAvgNone;
+    } else if ((W & (W - 1)) == 0) {
+        r.mode = kAvgMulPow2;   // s * 2^-k == s / W exactly for a power of two
+        r.inv_w = 1.0f / (float)W;
+    } else {
+        r.mode = kAvgDiv;
+        r.f_w = (float)W;
+    }
+    return ZERO1_OK;
+}
+
+zero1_status check_hparams(const zero1_hparams* hp)
+{
+    if (!hp) return fail(ZERO1_EINVAL, "hp is NULL");
+    if (!(hp->lr >= 0.0) || std::isinf(hp->lr)) return fail(ZERO1_EINVAL, "lr=%g must be finite and >= 0", hp->lr);
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(ZERO1_EINVAL, "beta1=%g must be in [0, 1)", hp->beta1);
+    if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(ZERO1_EINVAL, "beta2=%g must be in [0, 1)", hp->beta2);
+    if (!(hp->eps >= 0.0) || std::isinf(hp->eps)) return fail(ZERO1_EINVAL, "eps=%g must be finite and >= 0", hp->eps);
+    if (!(hp->weight_decay >= 0.0) || std::isinf(hp->weight_decay))
+        return fail(ZERO1_EINVAL, "weight_decay=%g must be finite and >= 0", hp->weight_decay);
+    if (!(hp->max_norm > 0.0)) return fail(ZERO1_EINVAL, "max_norm=%g must be > 0 (inf disables clipping)", hp->max_norm);
+    if (hp->step < 1) return fail(ZERO1_EINVAL, "step=%lld must be >= 1", (long long)hp->step);
+    return ZERO1_OK;
+}
+
+// The page's AdamW applies Python floats to fp32 tensors: each scalar is formed
+// in double and used as the nearest binary32 ("并行训练", section on mixed
+// precision and AdamW: step_size = lr*sqrt(1-beta2^t)/(1-beta1^t), decay 1-lr*wd).
+Scal scalars(const zero1_hparams* hp)
+{
+    Scal s;
+    s.b1 = (float)hp->beta1;
+    s.b2 = (float)hp->beta2;
+    s.a1 = (float)(1.0 - hp->beta1);
+    s.a2 = (float)(1.0 - hp->beta2);
+    s.eps = (float)hp->eps;
+    const double t = (double)hp->step;
+    const double bc1 = 1.0 - std::pow(hp->beta1, t);
+    const double bc2 = 1.0 - std::pow(hp->beta2, t);
+    s.sigma = (float)(hp->lr * std::sqrt(bc2) / bc1);
+    s.delta = (float)(1.0 - hp->lr * hp->weight_decay);
+    return s;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+    const char* what;
+    int idx;
+};
+
+// Reject any two overlapping non-empty byte ranges.
+zero1_status check_disjoint(std::vector<Range>& v)
+{
+    std::sort(v.begin(), v.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < v.size(); ++i)
+        if (v[i].lo < v[i - 1].hi)
+            return fail(ZERO1_EINVAL, "buffers overlap: %s[%d] and %s[%d]", v[i - 1].what, v[i - 1].idx,
+                        v[i].what, v[i].idx);
+    return ZERO1_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+int zero1_abi_version(void) { return ZERO1_ABI_VERSION; }
+
+const char* zero1_last_error(void) { return g_last_error.c_str(); }
+
+const char* zero1_status_string(int st)
+{
+    switch (st) {
+    case ZERO1_OK: return "ZERO1_OK";
+    case ZERO1_EINVAL: return "ZERO1_EINVAL";
+    case ZERO1_EWORKSPACE: return "ZERO1_EWORKSPACE";
+    case ZERO1_EHIP: return "ZERO1_EHIP";
+    case ZERO1_ENOTSUPPORTED: return "ZERO1_ENOTSUPPORTED";
+    default: return "ZERO1_UNKNOWN";
+    }
+}
+
+zero1_status zero1_shard_range(int64_t n_total, int W, int rank, int64_t* begin, int64_t* len)
+{
+    if (n_total < 0) return fail(ZERO1_EINVAL, "n_total=%lld is negative", (long long)n_total);
+    if (W < 1) return fail(ZERO1_EINVAL, "W=%d must be >= 1", W);
+    if (rank < 0 || rank >= W) return fail(ZERO1_EINVAL, "rank=%d must be in [0, %d)", rank, W);
+    if (!begin || !len) return fail(ZERO1_EINVAL, "begin/len outputs are NULL");
+    const int64_t S = n_total / W + (n_total % W != 0);
+    const int64_t b = std::min<int64_t>((int64_t)rank * S, n_total);
+    *begin = b;
+    *len = std::min<int64_t>(b + S, n_total) - b;
+    return ok();
+}
+
+size_t zero1_workspace_bytes(int64_t len, int W, uint32_t flags)
+{
+    (void)W;
+    size_t n = kGOffset;
+    if ((flags & ZERO1_STORE_G) && len > 0) n += round_up((size_t)len * sizeof(float), 256);
+    return n;
+}
+
+zero1_status zero1_shard_reduce(const uint16_t* const* grads, int W, int64_t begin, int64_t len,
+                                uint32_t flags, float* g_out, double* sumsq_out, void* ws,
+                                size_t ws_bytes, void* stream)
+{
+    Reduce r;
+    bool vec = false;
+    zero1_status st = check_grads(grads, W, begin, len, r, (flags & ZERO1_SUM_ONLY) != 0, vec);
+    if (st) return st;
+    if (!g_out && !sumsq_out) return fail(ZERO1_EINVAL, "g_out and sumsq_out are both NULL");
+    if (g_out) {
+        if (!aligned16(g_out)) vec = false;
+        std::vector<Range> rg;
+        rg.push_back({(uintptr_t)g_out, (uintptr_t)(g_out + len), "g_out", 0});
+        for (int w = 0; w < W; ++w)
+            rg.push_back({(uintptr_t)(grads[w] + begin), (uintptr_t)(grads[w] + begin + len), "grads", w});
+        if (len > 0 && (st = check_disjoint(rg))) return st;
+    }
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+    Ws w;
+    if (sumsq_out && (st = carve(ws, ws_bytes, zero1_workspace_bytes(len, W, 0), false, w))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (len == 0) {   // empty shard: the sum of no squares is 0 (a kernel, not a memset)
+        if (sumsq_out) Z1_HIP(launch_finalize(w.partials, 0, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+        return finish(s);
+    }
+    const int nb = grid_for(tiles(len, vec), d, kReducePerCu);
+    Z1_HIP(launch_reduce(r, len, vec, g_out, sumsq_out ? w.partials : nullptr, nb, s));
+    if (sumsq_out) Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+    return finish(s);
+}
+
+zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out, void* ws, size_t ws_bytes,
+                             void* stream)
+{
+    if (len < 0) return fail(ZERO1_EINVAL, "len=%lld is negative", (long long)len);
+    if (!sumsq_out) return fail(ZERO1_EINVAL, "sumsq_out is NULL");
+    if (!g && len > 0) return fail(ZERO1_EINVAL, "g is NULL");
+    zero1_status st;
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+    Ws w;
+    if ((st = carve(ws, ws_bytes, zero1_workspace_bytes(len, 1, 0), false, w))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (len == 0) {
+        Z1_HIP(launch_finalize(w.partials, 0, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+        return finish(s);
+    }
+    const bool vec = aligned16(g);
+    const int nb = grid_for(tiles(len, vec), d, kReducePerCu);
+    Z1_HIP(launch_sumsq(g, len, vec, w.partials, nb, s));
+    Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+    return finish(s);
+}
+
+zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int W, int64_t begin, int64_t len,
+                              float* master, void* m, void* v, uint16_t* param_bf16, const zero1_hparams* hp,
+                              const double* rank_sumsq, int n_ranks, uint32_t flags, zero1_norm_info* info_out,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    zero1_status st;
+    if ((st = check_hparams(hp))) return st;
+    if (len < 0) return fail(ZERO1_EINVAL, "len=%lld is negative", (long long)len);
+    if (n_ranks < 1) return fail(ZERO1_EINVAL, "n_ranks=%d must be >= 1", n_ranks);
+    if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
+    const bool mv_bf16 = (flags & ZERO1_MV_BF16) != 0;
+    Reduce r;
+    std::memset(&r, 0, sizeof r);
+    bool vec = true;
+    if (!g) {
+        if ((st = check_grads(grads, W, begin, len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
+    } else if (!aligned16(g)) {
+        vec = false;
+    }
+    if (len > 0 && (!master || !m || !v || !param_bf16))
+        return fail(ZERO1_EINVAL, "master, m, v and param_bf16 must be non-NULL");
+    const size_t mvb = mv_bf16 ? 2 : 4;
+    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(param_bf16)) vec = false;
+    if (len > 0) {
+        std::vector<Range> rg = {
+            {(uintptr_t)master, (uintptr_t)master + 4 * (size_t)len, "master", 0},
+            {(uintptr_t)m, (uintptr_t)m + mvb * (size_t)len, "m", 0},
+            {(uintptr_t)v, (uintptr_t)v + mvb * (size_t)len, "v", 0},
+            {(uintptr_t)param_bf16, (uintptr_t)param_bf16 + 2 * (size_t)len, "param_bf16", 0}};
+        if (g) rg.push_back({(uintptr_t)g, (uintptr_t)g + 4 * (size_t)len, "g", 0});
+        if ((st = check_disjoint(rg))) return st;
+    }
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+    Ws w;
+    if ((st = carve(ws, ws_bytes, zero1_workspace_bytes(len, W, 0), false, w))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Z1_HIP(launch_finalize(nullptr, 0, nullptr, rank_sumsq, n_ranks, hp->max_norm, w.info,
+                           reinterpret_cast<NormInfo*>(info_out), s));
+    if (len > 0) {
+        const Scal sc = scalars(hp);
+        const int nb = grid_for(tiles(len, vec), d, kAdamPerCu);
+        Z1_HIP(launch_adamw_flat(g, r, len, vec, mv_bf16, master, m, v, param_bf16, sc, w.info, nb, s));
+    }
+    return finish(s);
+}
+
+// ------------------------------------------------------------------ multi-tensor
+size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces)
+{
+    if (!pieces || n_pieces <= 0) return 0;
+    size_t chunks = 0;
+    for (int i = 0; i < n_pieces; ++i)
+        if (pieces[i].numel > 0) chunks += (size_t)((pieces[i].numel + kChunkElems - 1) / kChunkElems);
+    return round_up(sizeof(PieceDesc) * (size_t)n_pieces, 256) + sizeof(ChunkDesc) * chunks;
+}
+
+zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t flags, void* table,
+                            size_t table_bytes, zero1_plan* plan_out)
+{
+    if (!plan_out) return fail(ZERO1_EINVAL, "plan_out is NULL");
+    if (!pieces || n_pieces < 1) return fail(ZERO1_EINVAL, "need at least one piece");
+    const bool mv_bf16 = (flags & ZERO1_MV_BF16) != 0;
+    std::vector<int> order(n_pieces);
+    for (int i = 0; i < n_pieces; ++i) {
+        const zero1_piece& p = pieces[i];
+        if (p.numel <= 0) return fail(ZERO1_EINVAL, "piece %d: numel=%lld must be > 0", i, (long long)p.numel);
+        if (p.shard_offset < 0) return fail(ZERO1_EINVAL, "piece %d: negative shard_offset", i);
+        if (!p.param_bf16 || !p.master || !p.m || !p.v) return fail(ZERO1_EINVAL, "piece %d: NULL buffer", i);
+        if (p.numel > (int64_t)1 << 40) return fail(ZERO1_EINVAL, "piece %d: numel too large", i);
+        order[i] = i;
+    }
+    std::sort(order.begin(), order.end(),
+              [&](int a, int b) { return pieces[a].shard_offset < pieces[b].shard_offset; });
+    int64_t pos = 0;
+    for (int k = 0; k < n_pieces; ++k) {
+        const zero1_piece& p = pieces[order[k]];
+        if (p.shard_offset != pos)
+            return fail(ZERO1_EINVAL, "pieces do not tile the shard: piece %d starts at %lld, expected %lld",
+                        order[k], (long long)p.shard_offset, (long long)pos);
+        pos += p.numel;
+    }
+    const size_t mvb = mv_bf16 ? 2 : 4;
+    std::vector<Range> rg;
+    rg.reserve(4 * (size_t)n_pieces);
+    bool aligned = true;
+    for (int i = 0; i < n_pieces; ++i) {
+        const zero1_piece& p = pieces[i];
+        const size_t n = (size_t)p.numel;
+        rg.push_back({(uintptr_t)p.param_bf16, (uintptr_t)p.param_bf16 + 2 * n, "param_bf16", i});
+        rg.push_back({(uintptr_t)p.master, (uintptr_t)p.master + 4 * n, "master", i});
+        rg.push_back({(uintptr_t)p.m, (uintptr_t)p.m + mvb * n, "m", i});
+        rg.push_back({(uintptr_t)p.v, (uintptr_t)p.v + mvb * n, "v", i});
+        if (p.shard_offset % kVec || !aligned16(p.param_bf16) || !aligned16(p.master) || !aligned16(p.m) ||
+            !aligned16(p.v))
+            aligned = false;
+    }
+    zero1_status st;
+    if ((st = check_disjoint(rg))) return st;
+    const size_t need = zero1_mta_table_bytes(pieces, n_pieces);
+    if (!table) return fail(ZERO1_EWORKSPACE, "table is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(table) % 256) return fail(ZERO1_EWORKSPACE, "table must be 256-byte aligned");
+    if (table_bytes < need) return fail(ZERO1_EWORKSPACE, "table has %zu bytes, needs %zu", table_bytes, need);
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+
+    const size_t chunk_off = round_up(sizeof(PieceDesc) * (size_t)n_pieces, 256);
+    std::vector<char> host(need, 0);
+    PieceDesc* pd = reinterpret_cast<PieceDesc*>(host.data());
+    ChunkDesc* cd = reinterpret_cast<ChunkDesc*>(host.data() + chunk_off);
+    int64_t nc = 0;
+    for (int k = 0; k < n_pieces; ++k) {   // shard order, so chunk k covers shard positions in order
+        const zero1_piece& p = pieces[order[k]];
+        pd[k] = PieceDesc{p.numel, p.shard_offset, p.param_bf16, p.master, p.m, p.v};
+        for (int64_t off = 0; off < p.numel; off += kChunkElems) {
+            const int64_t l = std::min<int64_t>(kChunkElems, p.numel - off);
+            cd[nc++] = ChunkDesc{k, (int32_t)l, off};
+        }
+    }
+    if (nc > INT32_MAX) return fail(ZERO1_EINVAL, "too many chunks");
+    Z1_HIP(hipMemcpy(table, host.data(), need, hipMemcpyHostToDevice));
+    plan_out->table = table;
+    plan_out->shard_len = pos;
+    plan_out->n_pieces = n_pieces;
+    plan_out->n_chunks = (int32_t)nc;
+    plan_out->chunk_elems = kChunkElems;
+    plan_out->flags = flags & ZERO1_MV_BF16;
+    plan_out->aligned = aligned ? 1 : 0;
+    plan_out->reserved = 0;
+    return ok();
+}
+
+static bool use_store_g(uint32_t flags, int W)
+{
+    if (flags & ZERO1_STORE_G) return true;
+    if (flags & ZERO1_RECOMPUTE_G) return false;
+    return W > 4;   // 2W+34 bytes/param beats 4W+26 once W > 4
+}
+
+size_t zero1_mta_workspace_bytes(const zero1_plan* plan, int W, uint32_t flags)
+{
+    if (!plan) return 0;
+    return zero1_workspace_bytes(plan->shard_len, W, use_store_g(flags, W) ? ZERO1_STORE_G : 0);
+}
+
+zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
+                            const zero1_hparams* hp, double* rank_sumsq, int n_ranks, int my_rank,
+                            uint32_t flags, zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
+{
+    zero1_status st;
+    if (!plan || !plan->table) return fail(ZERO1_EINVAL, "plan is NULL or has no table");
+    if ((flags & ZERO1_STORE_G) && (flags & ZERO1_RECOMPUTE_G))
+        return fail(ZERO1_EINVAL, "ZERO1_STORE_G and ZERO1_RECOMPUTE_G are exclusive");
+    if ((st = check_hparams(hp))) return st;
+    if (n_ranks < 1 || my_rank < 0 || my_rank >= n_ranks)
+        return fail(ZERO1_EINVAL, "my_rank=%d must be in [0, n_ranks=%d)", my_rank, n_ranks);
+    if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
+    const int64_t len = plan->shard_len;
+    Reduce r;
+    bool vec = false;
+    if ((st = check_grads(grads, W, begin, len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
+    vec = vec && plan->aligned;
+    const bool store_g = use_store_g(flags, W);
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+    Ws w;
+    if ((st = carve(ws, ws_bytes, zero1_mta_workspace_bytes(plan, W, flags), store_g, w))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int nb1 = grid_for(tiles(len, vec), d, kReducePerCu);
+    Z1_HIP(launch_reduce(r, len, vec, w.g, w.partials, nb1, s));
+    Z1_HIP(launch_finalize(w.partials, nb1, rank_sumsq + my_rank, rank_sumsq, n_ranks, hp->max_norm, w.info,
+                           reinterpret_cast<NormInfo*>(info_out), s));
+    const char* tb = static_cast<const char*>(plan->table);
+    const PieceDesc* pd = reinterpret_cast<const PieceDesc*>(tb);
+    const ChunkDesc* cd = reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
+    const int nb2 = grid_for(plan->n_chunks, d, kAdamPerCu);
+    Z1_HIP(launch_adamw_mta(w.g, r, pd, cd, plan->n_chunks, vec, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp),
+                            w.info, nb2, s));
+    return finish(s);
+}
+
+}  // extern "C"

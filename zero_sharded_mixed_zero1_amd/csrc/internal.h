@@ -1,0 +1,90 @@
+// internal.h -- declarations shared by the C-ABI host code (api.cpp) and the
+// gfx950 kernels (kernels.hip) of libzero1.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace z1 {
+
+constexpr int kMaxW = 128;          // == ZERO1_MAX_W
+constexpr int kThreads = 256;       // threads per workgroup (4 waves of 64)
+constexpr int kVec = 8;             // elements per thread per 16-byte bf16 access
+constexpr int kMaxPartials = 8192;  // capacity of the per-workgroup norm partials
+constexpr int kChunkElems = 8192;   // multi-tensor chunk: 256 threads x 8 elements x 4
+
+// W gradient slice pointers, passed by value in the kernel arguments (1 KiB).
+struct GradPtrs {
+    const uint16_t* p[kMaxW];
+};
+
+// Per-step fp32 scalars, formed in fp64 on the host and rounded once.
+struct Scal {
+    float b1, b2, a1, a2, eps, sigma, delta;
+};
+
+// How the W-slice sum becomes g: keep it, multiply by the exact 2^-k (W a
+// power of two: identical to dividing), or divide by W.
+enum AvgMode : int { kAvgNone = 0, kAvgMulPow2 = 1, kAvgDiv = 2 };
+
+struct Reduce {
+    GradPtrs gp;   // already offset to the shard's first element
+    int W;
+    int mode;      // AvgMode
+    float inv_w;   // 2^-k for kAvgMulPow2
+    float f_w;     // (float)W for kAvgDiv
+};
+
+// Same layout as zero1_norm_info.
+struct NormInfo {
+    double sumsq_total;
+    double norm;
+    float clip_coef;
+    int32_t clip;
+    int32_t nonfinite;
+    int32_t reserved;
+};
+
+// Device-side piece descriptor (48 bytes) and chunk descriptor (16 bytes).
+struct PieceDesc {
+    int64_t numel;
+    int64_t shard_offset;
+    uint16_t* param;
+    float* master;
+    void* m;
+    void* v;
+};
+
+struct ChunkDesc {
+    int32_t piece;
+    int32_t len;
+    int64_t offset;   // element offset inside the piece
+};
+
+// ---- launchers (kernels.hip); each returns hipGetLastError() after launch.
+// Phase 1: g = reduce(slices) over [0, len); optional fp32 store of g and one
+// fp64 partial sum of squares per workgroup (nblocks of them).
+hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out,
+                         double* partials, int nblocks, hipStream_t s);
+// Sum of squares of an fp32 vector, one partial per workgroup.
+hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials,
+                        int nblocks, hipStream_t s);
+// One workgroup: add the partials in a fixed order into *q_out (if non-null);
+// then, if info != null, norm = sqrt(sum of rank_sumsq[0..n_ranks) in order)
+// and the clip decision for max_norm, into *info (and *info_copy if non-null).
+hipError_t launch_finalize(const double* partials, int nblocks, double* q_out,
+                           const double* rank_sumsq, int n_ranks, double max_norm,
+                           NormInfo* info, NormInfo* info_copy, hipStream_t s);
+// Phase 2 over a flat shard.  g == nullptr: recompute g from r.
+hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool vec,
+                             bool mv_bf16, float* master, void* m, void* v,
+                             uint16_t* param, const Scal& sc, const NormInfo* info,
+                             int nblocks, hipStream_t s);
+// Phase 2 over a multi-tensor plan.
+hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces,
+                            const ChunkDesc* chunks, int n_chunks, bool vec,
+                            bool mv_bf16, const Scal& sc, const NormInfo* info,
+                            int nblocks, hipStream_t s);
+
+}  // namespace z1
