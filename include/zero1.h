@@ -186,8 +186,8 @@ zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out,
  *   rank_sumsq  n_ranks doubles: every rank's partial sum of squares (this
  *               rank's included), added in rank order for the global norm.
  *   flags       ZERO1_MV_BF16, ZERO1_SUM_ONLY (with g == NULL).
- *   info_out    one zero1_norm_info (device) or NULL.
- *   ws          zero1_workspace_bytes(len, W, 0) bytes.
+ *   info_out    one zero1_norm_info (device) or NULL; written even when len == 0.
+ * Needs no workspace: every workgroup forms the norm from rank_sumsq itself.
  * Per element, with c the clip coefficient when clipping:
  *   g' = g*c;  m = b1*m + a1*g';  v = b2*v + a2*(g'*g');
  *   p = p - sigma*(m / (sqrt(v) + eps));  p = p*delta;  param = bf16(p)
@@ -200,7 +200,7 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads,
                               uint16_t* param_bf16, const zero1_hparams* hp,
                               const double* rank_sumsq, int n_ranks,
                               uint32_t flags, zero1_norm_info* info_out,
-                              void* ws, size_t ws_bytes, void* stream);
+                              void* stream);
 
 /* ---------------------------------------------------------------- fused step
  * Multi-tensor apply over a ragged per-tensor list (the parameter list the
@@ -213,20 +213,35 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads,
  *   table_bytes long).  Synchronous: call once per tensor-list layout and
  *   reuse the plan for every step.  `flags` may hold ZERO1_MV_BF16.
  * zero1_mta_workspace_bytes: step workspace for this plan and W.
- * zero1_mta_step: the whole step (1-5) for rank my_rank:
- *   grads, W, begin  as for zero1_shard_reduce (the shard's gradient slices).
- *   rank_sumsq  n_ranks doubles: the other ranks' partials on entry; entry
- *               my_rank is overwritten with this rank's partial before the
- *               norm is formed (the partials of the other ranks are the only
- *               value a multi-GPU run would have to exchange mid-step).
- *   flags       ZERO1_STORE_G / ZERO1_RECOMPUTE_G / ZERO1_SUM_ONLY
- *               (ZERO1_MV_BF16 comes from the plan).
- *   Results are bit-identical to zero1_shard_reduce + zero1_adamw_step. */
+ * zero1_mta_reduce: steps 1-2 for this rank: reduces the shard's gradient
+ *   slices (grads, W, begin as for zero1_shard_reduce) and writes this rank's
+ *   partial sum of squares to *sumsq_out (device).  With ZERO1_STORE_G the
+ *   fp32 g is kept in the workspace for zero1_mta_update.
+ * zero1_mta_update: steps 3-5: forms the global norm from rank_sumsq
+ *   (n_ranks doubles, added in rank order), clips, and updates every piece.
+ *   Must get the same grads, W, begin, plan, flags and workspace as the
+ *   zero1_mta_reduce it follows.  A multi-GPU caller exchanges the ranks'
+ *   partials between the two calls (one double per rank: the only data the
+ *   step needs from other ranks once the gradients are reduced).
+ * zero1_mta_step: zero1_mta_reduce with sumsq_out = rank_sumsq + my_rank,
+ *   then zero1_mta_update: the whole step (1-5) for rank my_rank when the
+ *   other ranks' partials are already in rank_sumsq.
+ *   flags: ZERO1_STORE_G / ZERO1_RECOMPUTE_G / ZERO1_SUM_ONLY (ZERO1_MV_BF16
+ *   comes from the plan).  Results are bit-identical to zero1_shard_reduce +
+ *   zero1_adamw_step on the same shard. */
 size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces);
 zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces,
                             uint32_t flags, void* table, size_t table_bytes,
                             zero1_plan* plan_out);
 size_t zero1_mta_workspace_bytes(const zero1_plan* plan, int W, uint32_t flags);
+zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin,
+                              const zero1_plan* plan, double* sumsq_out,
+                              uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin,
+                              const zero1_plan* plan, const zero1_hparams* hp,
+                              const double* rank_sumsq, int n_ranks, uint32_t flags,
+                              zero1_norm_info* info_out, void* ws, size_t ws_bytes,
+                              void* stream);
 zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
                             const zero1_plan* plan, const zero1_hparams* hp,
                             double* rank_sumsq, int n_ranks, int my_rank,

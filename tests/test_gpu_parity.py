@@ -167,10 +167,10 @@ def test_adamw_step_flat_parity(env, mv_bf16, source):
                 torch.cuda.synchronize()
                 assert rel_close(sq.item(), rs[0], NORM_TOL)
                 z.adamw_step(gbuf, None, 0, length, gm, gmm, gvv, gp, hp, rsd, 3,
-                             flags=z.MV_BF16 if mv_bf16 else 0, info_out=info, ws=ws)
+                             flags=z.MV_BF16 if mv_bf16 else 0, info_out=info)
             else:
                 z.adamw_step(None, gd, offset, length, gm, gmm, gvv, gp, hp, rsd, 3,
-                             flags=z.MV_BF16 if mv_bf16 else 0, info_out=info, ws=ws)
+                             flags=z.MV_BF16 if mv_bf16 else 0, info_out=info)
             torch.cuda.synchronize()
             ni = info.cpu().numpy()
             assert ni[1] == oinfo.norm                        # same partials in, same norm out
@@ -301,7 +301,7 @@ def test_mta_equals_reduce_plus_adamw(env):
         rs2 = rs1.clone()
         z.mta_step(gd, b0, a.plan, hp_at(t), rs1, W, r, flags=z.STORE_G, ws=ws1)
         z.shard_reduce(gd, b0, S, g_out=g, sumsq_out=rs2[r:r + 1], ws=ws2)
-        z.adamw_step(g, None, 0, S, fm, fmm, fvv, fp, hp_at(t), rs2, W, ws=ws2)
+        z.adamw_step(g, None, 0, S, fm, fmm, fvv, fp, hp_at(t), rs2, W)
         torch.cuda.synchronize()
         assert rs1[r].item() == rs2[r].item()
     master, m, v, param = a.gather()
@@ -366,7 +366,7 @@ def test_nonfinite_gradient_propagates(env):
         info = torch.zeros(4, dtype=torch.float64, device=dev)
         z.shard_reduce(gd, 0, N, sumsq_out=rsd, ws=ws)
         z.adamw_step(None, gd, 0, N, gm, gmm, gvv, gp, hp_at(1, max_norm=max_norm), rsd, 1,
-                     info_out=info, ws=ws)
+                     info_out=info)
         torch.cuda.synchronize()
         ni = info.cpu().numpy()
         assert np.isnan(ni[1]) and np.isnan(oi.norm)
@@ -395,7 +395,7 @@ def test_bf16_stagnation_on_gpu(env):
     for t in range(1, 1001):
         hp = hp_at(t, weight_decay=0.0, max_norm=math.inf)
         z.shard_reduce(gd, 0, n, sumsq_out=rsd, ws=ws)
-        z.adamw_step(None, gd, 0, n, gm, gmm, gvv, gp, hp, rsd, 1, ws=ws)
+        z.adamw_step(None, gd, 0, n, gm, gmm, gvv, gp, hp, rsd, 1)
         oracle.step([g], omaster, om, ov, oparam, hp, np.zeros(1), 0)
     torch.cuda.synchronize()
     assert_f32_equal(gm.cpu().numpy(), omaster, "master after 1000 steps")

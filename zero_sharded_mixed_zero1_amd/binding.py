@@ -83,7 +83,7 @@ def lib():
         L.zero1_grad_norm.argtypes = [P, i64, P, P, szt, P]
         L.zero1_grad_norm.restype = i32
         L.zero1_adamw_step.argtypes = [P, P, i32, i64, i64, P, P, P, P, ctypes.POINTER(HParams),
-                                       P, i32, u32, P, P, szt, P]
+                                       P, i32, u32, P, P]
         L.zero1_adamw_step.restype = i32
         L.zero1_mta_table_bytes.argtypes = [ctypes.POINTER(Piece), i32]
         L.zero1_mta_table_bytes.restype = szt
@@ -91,6 +91,11 @@ def lib():
         L.zero1_mta_plan.restype = i32
         L.zero1_mta_workspace_bytes.argtypes = [ctypes.POINTER(Plan), i32, u32]
         L.zero1_mta_workspace_bytes.restype = szt
+        L.zero1_mta_reduce.argtypes = [P, i32, i64, ctypes.POINTER(Plan), P, u32, P, szt, P]
+        L.zero1_mta_reduce.restype = i32
+        L.zero1_mta_update.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
+                                       P, i32, u32, P, P, szt, P]
+        L.zero1_mta_update.restype = i32
         L.zero1_mta_step.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                      P, i32, i32, u32, P, P, szt, P]
         L.zero1_mta_step.restype = i32
@@ -185,15 +190,14 @@ def grad_norm(g, length: int, sumsq_out, ws=None, ws_bytes=None, stream=None):
 
 
 def adamw_step(g, grads, begin: int, length: int, master, m, v, param_bf16, hp, rank_sumsq,
-               n_ranks: int, flags: int = 0, info_out=None, ws=None, ws_bytes=None, stream=None):
+               n_ranks: int, flags: int = 0, info_out=None, stream=None):
     grads = list(grads) if grads is not None else []
     arr = _ptrs(grads) if grads else None
-    w, wb = _ws(ws, ws_bytes)
     h = _hp(hp)
     _check(lib().zero1_adamw_step(_addr(g), ctypes.cast(arr, P) if arr is not None else None,
                                   len(grads), begin, length, _addr(master), _addr(m), _addr(v),
                                   _addr(param_bf16), ctypes.byref(h), _addr(rank_sumsq), n_ranks,
-                                  flags, _addr(info_out), w, wb, _stream(stream)))
+                                  flags, _addr(info_out), _stream(stream)))
 
 
 def _pieces(pieces):
@@ -225,6 +229,24 @@ def mta_plan(pieces, table, table_bytes=None, flags: int = 0) -> Plan:
 
 def mta_workspace_bytes(plan: Plan, W: int, flags: int = 0) -> int:
     return lib().zero1_mta_workspace_bytes(ctypes.byref(plan), W, flags)
+
+
+def mta_reduce(grads, begin: int, plan: Plan, sumsq_out, flags: int = 0, ws=None, ws_bytes=None,
+               stream=None):
+    arr = _ptrs(grads)
+    w, wb = _ws(ws, ws_bytes)
+    _check(lib().zero1_mta_reduce(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
+                                  _addr(sumsq_out), flags, w, wb, _stream(stream)))
+
+
+def mta_update(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, flags: int = 0,
+               info_out=None, ws=None, ws_bytes=None, stream=None):
+    arr = _ptrs(grads)
+    w, wb = _ws(ws, ws_bytes)
+    h = _hp(hp)
+    _check(lib().zero1_mta_update(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
+                                  ctypes.byref(h), _addr(rank_sumsq), n_ranks, flags,
+                                  _addr(info_out), w, wb, _stream(stream)))
 
 
 def mta_step(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, my_rank: int,

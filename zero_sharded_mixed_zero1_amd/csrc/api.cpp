@@ -287,12 +287,12 @@ zero1_status zero1_shard_reduce(const uint16_t* const* grads, int W, int64_t beg
     if (sumsq_out && (st = carve(ws, ws_bytes, zero1_workspace_bytes(len, W, 0), false, w))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (len == 0) {   // empty shard: the sum of no squares is 0 (a kernel, not a memset)
-        if (sumsq_out) Z1_HIP(launch_finalize(w.partials, 0, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+        if (sumsq_out) Z1_HIP(launch_finalize(w.partials, 0, sumsq_out, s));
         return finish(s);
     }
     const int nb = grid_for(tiles(len, vec), d, kReducePerCu);
     Z1_HIP(launch_reduce(r, len, vec, g_out, sumsq_out ? w.partials : nullptr, nb, s));
-    if (sumsq_out) Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+    if (sumsq_out) Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, s));
     return finish(s);
 }
 
@@ -309,20 +309,20 @@ zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out, voi
     if ((st = carve(ws, ws_bytes, zero1_workspace_bytes(len, 1, 0), false, w))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (len == 0) {
-        Z1_HIP(launch_finalize(w.partials, 0, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+        Z1_HIP(launch_finalize(w.partials, 0, sumsq_out, s));
         return finish(s);
     }
     const bool vec = aligned16(g);
     const int nb = grid_for(tiles(len, vec), d, kReducePerCu);
     Z1_HIP(launch_sumsq(g, len, vec, w.partials, nb, s));
-    Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, nullptr, 0, 0.0, nullptr, nullptr, s));
+    Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, s));
     return finish(s);
 }
 
 zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int W, int64_t begin, int64_t len,
                               float* master, void* m, void* v, uint16_t* param_bf16, const zero1_hparams* hp,
                               const double* rank_sumsq, int n_ranks, uint32_t flags, zero1_norm_info* info_out,
-                              void* ws, size_t ws_bytes, void* stream)
+                              void* stream)
 {
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
@@ -353,16 +353,12 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
     }
     DevInfo d;
     if ((st = current_device(d))) return st;
-    Ws w;
-    if ((st = carve(ws, ws_bytes, zero1_workspace_bytes(len, W, 0), false, w))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Z1_HIP(launch_finalize(nullptr, 0, nullptr, rank_sumsq, n_ranks, hp->max_norm, w.info,
-                           reinterpret_cast<NormInfo*>(info_out), s));
-    if (len > 0) {
-        const Scal sc = scalars(hp);
-        const int nb = grid_for(tiles(len, vec), d, kAdamPerCu);
-        Z1_HIP(launch_adamw_flat(g, r, len, vec, mv_bf16, master, m, v, param_bf16, sc, w.info, nb, s));
-    }
+    // always launched (also for len == 0) so that info_out is written
+    const Scal sc = scalars(hp);
+    const int nb = grid_for(tiles(len, vec), d, kAdamPerCu);
+    Z1_HIP(launch_adamw_flat(g, r, len, vec, mv_bf16, master, m, v, param_bf16, sc, rank_sumsq, n_ranks,
+                             hp->max_norm, reinterpret_cast<NormInfo*>(info_out), nb, s));
     return finish(s);
 }
 
@@ -464,40 +460,73 @@ size_t zero1_mta_workspace_bytes(const zero1_plan* plan, int W, uint32_t flags)
     return zero1_workspace_bytes(plan->shard_len, W, use_store_g(flags, W) ? ZERO1_STORE_G : 0);
 }
 
-zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
-                            const zero1_hparams* hp, double* rank_sumsq, int n_ranks, int my_rank,
-                            uint32_t flags, zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
+// Shared checks of the two mta phases.
+static zero1_status mta_common(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
+                               uint32_t flags, void* ws, size_t ws_bytes, Reduce& r, bool& vec, bool& store_g,
+                               DevInfo& d, Ws& w)
 {
     zero1_status st;
     if (!plan || !plan->table) return fail(ZERO1_EINVAL, "plan is NULL or has no table");
     if ((flags & ZERO1_STORE_G) && (flags & ZERO1_RECOMPUTE_G))
         return fail(ZERO1_EINVAL, "ZERO1_STORE_G and ZERO1_RECOMPUTE_G are exclusive");
+    if ((st = check_grads(grads, W, begin, plan->shard_len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
+    vec = vec && plan->aligned;
+    store_g = use_store_g(flags, W);
+    if ((st = current_device(d))) return st;
+    return carve(ws, ws_bytes, zero1_mta_workspace_bytes(plan, W, flags), store_g, w);
+}
+
+zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
+                              double* sumsq_out, uint32_t flags, void* ws, size_t ws_bytes, void* stream)
+{
+    Reduce r;
+    bool vec = false, store_g = false;
+    DevInfo d;
+    Ws w;
+    if (!sumsq_out) return fail(ZERO1_EINVAL, "sumsq_out is NULL");
+    zero1_status st = mta_common(grads, W, begin, plan, flags, ws, ws_bytes, r, vec, store_g, d, w);
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int nb = grid_for(tiles(plan->shard_len, vec), d, kReducePerCu);
+    Z1_HIP(launch_reduce(r, plan->shard_len, vec, w.g, w.partials, nb, s));
+    Z1_HIP(launch_finalize(w.partials, nb, sumsq_out, s));
+    return finish(s);
+}
+
+zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
+                              const zero1_hparams* hp, const double* rank_sumsq, int n_ranks, uint32_t flags,
+                              zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
+{
+    zero1_status st;
+    if ((st = check_hparams(hp))) return st;
+    if (n_ranks < 1) return fail(ZERO1_EINVAL, "n_ranks=%d must be >= 1", n_ranks);
+    if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
+    Reduce r;
+    bool vec = false, store_g = false;
+    DevInfo d;
+    Ws w;
+    if ((st = mta_common(grads, W, begin, plan, flags, ws, ws_bytes, r, vec, store_g, d, w))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const char* tb = static_cast<const char*>(plan->table);
+    const PieceDesc* pd = reinterpret_cast<const PieceDesc*>(tb);
+    const ChunkDesc* cd = reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
+    const int nb = grid_for(plan->n_chunks, d, kAdamPerCu);
+    Z1_HIP(launch_adamw_mta(w.g, r, pd, cd, plan->n_chunks, vec, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp),
+                            rank_sumsq, n_ranks, hp->max_norm, reinterpret_cast<NormInfo*>(info_out), nb, s));
+    return finish(s);
+}
+
+zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
+                            const zero1_hparams* hp, double* rank_sumsq, int n_ranks, int my_rank,
+                            uint32_t flags, zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
+{
+    zero1_status st;
     if ((st = check_hparams(hp))) return st;
     if (n_ranks < 1 || my_rank < 0 || my_rank >= n_ranks)
         return fail(ZERO1_EINVAL, "my_rank=%d must be in [0, n_ranks=%d)", my_rank, n_ranks);
     if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
-    const int64_t len = plan->shard_len;
-    Reduce r;
-    bool vec = false;
-    if ((st = check_grads(grads, W, begin, len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
-    vec = vec && plan->aligned;
-    const bool store_g = use_store_g(flags, W);
-    DevInfo d;
-    if ((st = current_device(d))) return st;
-    Ws w;
-    if ((st = carve(ws, ws_bytes, zero1_mta_workspace_bytes(plan, W, flags), store_g, w))) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int nb1 = grid_for(tiles(len, vec), d, kReducePerCu);
-    Z1_HIP(launch_reduce(r, len, vec, w.g, w.partials, nb1, s));
-    Z1_HIP(launch_finalize(w.partials, nb1, rank_sumsq + my_rank, rank_sumsq, n_ranks, hp->max_norm, w.info,
-                           reinterpret_cast<NormInfo*>(info_out), s));
-    const char* tb = static_cast<const char*>(plan->table);
-    const PieceDesc* pd = reinterpret_cast<const PieceDesc*>(tb);
-    const ChunkDesc* cd = reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
-    const int nb2 = grid_for(plan->n_chunks, d, kAdamPerCu);
-    Z1_HIP(launch_adamw_mta(w.g, r, pd, cd, plan->n_chunks, vec, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp),
-                            w.info, nb2, s));
-    return finish(s);
+    if ((st = zero1_mta_reduce(grads, W, begin, plan, rank_sumsq + my_rank, flags, ws, ws_bytes, stream))) return st;
+    return zero1_mta_update(grads, W, begin, plan, hp, rank_sumsq, n_ranks, flags, info_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -70,21 +70,21 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out,
 // Sum of squares of an fp32 vector, one partial per workgroup.
 hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials,
                         int nblocks, hipStream_t s);
-// One workgroup: add the partials in a fixed order into *q_out (if non-null);
-// then, if info != null, norm = sqrt(sum of rank_sumsq[0..n_ranks) in order)
-// and the clip decision for max_norm, into *info (and *info_copy if non-null).
-hipError_t launch_finalize(const double* partials, int nblocks, double* q_out,
-                           const double* rank_sumsq, int n_ranks, double max_norm,
-                           NormInfo* info, NormInfo* info_copy, hipStream_t s);
-// Phase 2 over a flat shard.  g == nullptr: recompute g from r.
+// One workgroup: add the per-workgroup partials in a fixed order into *q_out.
+hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, hipStream_t s);
+// Phase 2 over a flat shard.  g == nullptr: recompute g from r.  Every
+// workgroup first forms the global norm from rank_sumsq[0..n_ranks) (in rank
+// order) and the clip decision for max_norm; workgroup 0 writes it to info_out.
 hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool vec,
                              bool mv_bf16, float* master, void* m, void* v,
-                             uint16_t* param, const Scal& sc, const NormInfo* info,
+                             uint16_t* param, const Scal& sc, const double* rank_sumsq,
+                             int n_ranks, double max_norm, NormInfo* info_out,
                              int nblocks, hipStream_t s);
-// Phase 2 over a multi-tensor plan.
+// Phase 2 over a multi-tensor plan (same prologue).
 hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces,
                             const ChunkDesc* chunks, int n_chunks, bool vec,
-                            bool mv_bf16, const Scal& sc, const NormInfo* info,
+                            bool mv_bf16, const Scal& sc, const double* rank_sumsq,
+                            int n_ranks, double max_norm, NormInfo* info_out,
                             int nblocks, hipStream_t s);
 
 }  // namespace z1

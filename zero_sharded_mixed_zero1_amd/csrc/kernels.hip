@@ -188,10 +188,10 @@ __global__ __launch_bounds__(kThreads) void sumsq_kernel(const float* __restrict
 }
 
 // ------------------------------------------------------------- finalize
+// One workgroup adds the per-workgroup partials of phase 1 in a fixed order:
+// each lane sums a strided subset sequentially, then a fixed LDS tree.
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const double* __restrict__ partials, int nb,
-                                                            double* q_out, const double* rank_sumsq,
-                                                            int n_ranks, double max_norm, NormInfo* info,
-                                                            NormInfo* info_copy)
+                                                            double* __restrict__ q_out)
 {
     __shared__ double sh[kThreads];
     double a = 0.0;
@@ -202,12 +202,18 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const double* __rest
         if ((int)threadIdx.x < s) sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + s];
         __syncthreads();
     }
-    if (threadIdx.x != 0) return;
-    if (q_out) *q_out = sh[0];
-    if (!info) return;
+    if (threadIdx.x == 0) *q_out = sh[0];
+}
+
+// Global norm and clip decision from the ranks' partial sums of squares
+// ("训练循环与 checkpoint": clip all gradients as one vector when the L2 norm
+// exceeds max_norm).  The partials are added in rank order, so every
+// workgroup that evaluates this gets the same bits.
+__device__ __forceinline__ NormInfo clip_info(const double* rank_sumsq, int n_ranks, double max_norm)
+{
+    NormInfo ni;
     double tot = 0.0;
     for (int q = 0; q < n_ranks; ++q) tot = tot + rank_sumsq[q];
-    NormInfo ni;
     ni.sumsq_total = tot;
     ni.norm = sqrt(tot);
     if (ni.norm > max_norm) {
@@ -219,8 +225,28 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const double* __rest
     }
     ni.nonfinite = (isnan(ni.norm) || isinf(ni.norm)) ? 1 : 0;
     ni.reserved = 0;
-    *info = ni;
-    if (info_copy) *info_copy = ni;
+    return ni;
+}
+
+// Prologue of every update kernel: lane 0 forms the clip decision, workgroup 0
+// publishes it, and the whole workgroup reads it from LDS.
+struct ClipArgs {
+    const double* rank_sumsq;
+    int n_ranks;
+    double max_norm;
+    NormInfo* info_out;   // may be null
+};
+
+__device__ __forceinline__ void block_clip(const ClipArgs& ca, bool& clip, float& coef)
+{
+    __shared__ NormInfo sh;
+    if (threadIdx.x == 0) {
+        sh = clip_info(ca.rank_sumsq, ca.n_ranks, ca.max_norm);
+        if (blockIdx.x == 0 && ca.info_out) *ca.info_out = sh;
+    }
+    __syncthreads();
+    clip = sh.clip != 0;
+    coef = sh.clip_coef;
 }
 
 // ------------------------------------------------------------- phase 2
@@ -333,10 +359,11 @@ __global__ __launch_bounds__(kThreads) void adamw_flat_kernel(const float* __res
                                                               int64_t len, float* __restrict__ master,
                                                               void* __restrict__ m, void* __restrict__ v,
                                                               uint16_t* __restrict__ param, Scal c,
-                                                              const NormInfo* __restrict__ info)
+                                                              ClipArgs ca)
 {
-    const bool clip = info->clip != 0;
-    const float coef = info->clip_coef;
+    bool clip;
+    float coef;
+    block_clip(ca, clip, coef);
     const int64_t tile = (int64_t)kThreads * V;
     const int64_t ntiles = (len + tile - 1) / tile;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
@@ -352,10 +379,11 @@ __global__ __launch_bounds__(kThreads) void adamw_mta_kernel(const float* __rest
                                                              const PieceDesc* __restrict__ pieces,
                                                              const ChunkDesc* __restrict__ chunks,
                                                              int n_chunks, Scal c,
-                                                             const NormInfo* __restrict__ info)
+                                                             ClipArgs ca)
 {
-    const bool clip = info->clip != 0;
-    const float coef = info->clip_coef;
+    bool clip;
+    float coef;
+    block_clip(ca, clip, coef);
     for (int k = blockIdx.x; k < n_chunks; k += gridDim.x) {
         const ChunkDesc ch = chunks[k];
         const PieceDesc pc = pieces[ch.piece];
@@ -404,20 +432,20 @@ hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials,
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, const double* rank_sumsq,
-                           int n_ranks, double max_norm, NormInfo* info, NormInfo* info_copy, hipStream_t s)
+hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, hipStream_t s)
 {
-    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials, nblocks, q_out,
-                       rank_sumsq, n_ranks, max_norm, info, info_copy);
+    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials, nblocks, q_out);
     return hipGetLastError();
 }
 
 hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool vec, bool mv_bf16,
                              float* master, void* m, void* v, uint16_t* param, const Scal& sc,
-                             const NormInfo* info, int nblocks, hipStream_t s)
+                             const double* rank_sumsq, int n_ranks, double max_norm, NormInfo* info_out,
+                             int nblocks, hipStream_t s)
 {
     const dim3 grid(nblocks), block(kThreads);
-#define Z1_FLAT(V, GS, MV) hipLaunchKernelGGL((adamw_flat_kernel<V, GS, MV>), grid, block, 0, s, g, r, len, master, m, v, param, sc, info)
+    const ClipArgs ca{rank_sumsq, n_ranks, max_norm, info_out};
+#define Z1_FLAT(V, GS, MV) hipLaunchKernelGGL((adamw_flat_kernel<V, GS, MV>), grid, block, 0, s, g, r, len, master, m, v, param, sc, ca)
     const int gs = g ? 0 : 1;
     if (vec) {
         if (gs == 0) { if (mv_bf16) Z1_FLAT(kVec, 0, true); else Z1_FLAT(kVec, 0, false); }
@@ -431,11 +459,12 @@ hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool 
 }
 
 hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks,
-                            int n_chunks, bool vec, bool mv_bf16, const Scal& sc, const NormInfo* info,
-                            int nblocks, hipStream_t s)
+                            int n_chunks, bool vec, bool mv_bf16, const Scal& sc, const double* rank_sumsq,
+                            int n_ranks, double max_norm, NormInfo* info_out, int nblocks, hipStream_t s)
 {
     const dim3 grid(nblocks), block(kThreads);
-#define Z1_MTA(V, GS, MV) hipLaunchKernelGGL((adamw_mta_kernel<V, GS, MV>), grid, block, 0, s, g, r, pieces, chunks, n_chunks, sc, info)
+    const ClipArgs ca{rank_sumsq, n_ranks, max_norm, info_out};
+#define Z1_MTA(V, GS, MV) hipLaunchKernelGGL((adamw_mta_kernel<V, GS, MV>), grid, block, 0, s, g, r, pieces, chunks, n_chunks, sc, ca)
     const int gs = g ? 0 : 1;
     if (vec) {
         if (gs == 0) { if (mv_bf16) Z1_MTA(kVec, 0, true); else Z1_MTA(kVec, 0, false); }
