@@ -37,9 +37,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 UPDATE_KERNEL = "adamw_mta_kernel"
+ONCHIP_KERNEL = "onchip_step_kernel"
 REDUCE_KERNEL = "reduce_kernel"
 CALIB_BYTES = 1 << 30          # the plain copy used to scale the PMC byte counters
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_mta_gpt2small_w8_pmc.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "zero1_step_gpt2small_w8_pmc.txt")
 
 
 def kernel_source_hash() -> str:
@@ -121,21 +122,30 @@ def hp(cfg, t):
 
 
 # ---------------------------------------------------------------------- the step
-def run_steps(torch, z, cfg, st, flags, k0, k1, events=None):
-    """Steps k0..k1-1 (t = k+1), rotating through the copies."""
+def run_steps(z, cfg, st, flags, k0, k1, events=None):
+    """Steps k0..k1-1 (t = k+1), rotating through the copies.  With the default
+    design a step is one zero1_mta_step call (a single launch when the shard
+    fits on chip); with an explicit two-phase design it is zero1_mta_reduce +
+    zero1_mta_update.  events[i] = (start, end) brackets the step's dominant
+    kernel: the whole single-launch step, or the update of the two-phase step."""
     W, rank = st["W"], st["rank"]
     copies = st["copies"]
+    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
     for k in range(k0, k1):
         c = copies[k % len(copies)]
         h = hp(cfg, k + 1)
-        if events is not None:
-            events[k - k0][0].record()
-        z.mta_reduce(c.grads, c.begin, c.plan, c.rsd[rank:rank + 1], flags=flags, ws=c.ws)
-        if events is not None:
-            events[k - k0][1].record()
-        z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
-        if events is not None:
-            events[k - k0][2].record()
+        ev = events[k - k0] if events is not None else None
+        if two_phase:
+            z.mta_reduce(c.grads, c.begin, c.plan, c.rsd[rank:rank + 1], flags=flags, ws=c.ws)
+            if ev:
+                ev[0].record()
+            z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
+        else:
+            if ev:
+                ev[0].record()
+            z.mta_step(c.grads, c.begin, c.plan, h, c.rsd, W, rank, flags=flags, ws=c.ws)
+        if ev:
+            ev[1].record()
 
 
 # ---------------------------------------------------------------------- CPU baseline
@@ -186,7 +196,10 @@ def read_pmc_dir(d):
     return {k: list(v.values()) for k, v in out.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir, out_path):
+def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL):
+    """Median FETCH_SIZE / WRITE_SIZE per dispatch of `kernel`, scaled by what
+    the same counters read for a torch.neg over CALIB_BYTES (a plain copy:
+    CALIB_BYTES read, CALIB_BYTES written), appended to out_path."""
     fetch, write = read_pmc_dir(fetch_dir), read_pmc_dir(write_dir)
 
     def pick(d, key):
@@ -196,33 +209,31 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
         raise SystemExit(f"no kernel matching {key!r} in {list(d)[:10]}")
 
     import statistics as stt
-    res = {}
-    for tag, key in (("update", UPDATE_KERNEL), ("reduce", REDUCE_KERNEL), ("calib", "neg")):
-        kf, vf = pick(fetch, key if tag != "calib" else "neg")
-        kw, vw = pick(write, key if tag != "calib" else "neg")
-        res[tag] = dict(kernel=kf, fetch_kib=stt.median(vf), write_kib=stt.median(vw), n=len(vf))
-    cal = res["calib"]
-    f_scale = (CALIB_BYTES / 1024.0) / cal["fetch_kib"]
-    w_scale = (CALIB_BYTES / 1024.0) / cal["write_kib"]
+    kf, vf = pick(fetch, kernel)
+    _, vw = pick(write, kernel)
+    _, cf = pick(fetch, "neg_kernel")
+    _, cw = pick(write, "neg_kernel")
+    f_scale = (CALIB_BYTES / 1024.0) / stt.median(cf)
+    w_scale = (CALIB_BYTES / 1024.0) / stt.median(cw)
+    fb = stt.median(vf) * 1024 * f_scale
+    wb = stt.median(vw) * 1024 * w_scale
     lines = [f"kernel_source_hash = {kernel_source_hash()}",
-             f"calibration: torch.neg of {CALIB_BYTES} bytes fp32 -> FETCH_SIZE {cal['fetch_kib']:.1f} KiB, "
-             f"WRITE_SIZE {cal['write_kib']:.1f} KiB; scale fetch {f_scale:.4f}, write {w_scale:.4f}"]
-    for tag in ("update", "reduce"):
-        r = res[tag]
-        fb = r["fetch_kib"] * 1024 * f_scale
-        wb = r["write_kib"] * 1024 * w_scale
-        lines.append(f"{tag}: {r['kernel'][:90]}")
-        lines.append(f"{tag}_fetch_bytes = {fb:.0f}")
-        lines.append(f"{tag}_write_bytes = {wb:.0f}")
-        lines.append(f"{tag}_dispatches = {r['n']}")
+             f"dominant_kernel = {kernel}",
+             f"# {kf[:110]}",
+             f"# calibration: torch.neg over {CALIB_BYTES} B fp32 reads FETCH_SIZE {stt.median(cf):.1f} KiB "
+             f"and WRITE_SIZE {stt.median(cw):.1f} KiB; scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+             f"# raw per dispatch (median of {len(vf)}): FETCH_SIZE {stt.median(vf):.1f} KiB, "
+             f"WRITE_SIZE {stt.median(vw):.1f} KiB",
+             f"dominant_fetch_bytes = {fb:.0f}",
+             f"dominant_write_bytes = {wb:.0f}"]
     with open(out_path, "a") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def traffic_from_summary(path):
-    """Counter bytes per update launch from the committed summary, or None if
-    the kernels changed since the counters were taken."""
+def traffic_from_summary(path, kernel):
+    """Counter bytes per launch of `kernel` from the committed summary, or None
+    if the kernels changed since the counters were taken."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -230,10 +241,10 @@ def traffic_from_summary(path):
         if "=" in line and not line.startswith("#"):
             k, v = (s.strip() for s in line.split("=", 1))
             kv[k] = v
-    if kv.get("kernel_source_hash") != kernel_source_hash():
+    if kv.get("kernel_source_hash") != kernel_source_hash() or kv.get("dominant_kernel") != kernel:
         return None
     try:
-        return float(kv["update_fetch_bytes"]) + float(kv["update_write_bytes"])
+        return float(kv["dominant_fetch_bytes"]) + float(kv["dominant_write_bytes"])
     except (KeyError, ValueError):
         return None
 
@@ -245,7 +256,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C2")
-    ap.add_argument("--design", choices=["auto", "store", "recompute"], default="auto")
+    ap.add_argument("--design", choices=["auto", "onchip", "store", "recompute"], default="auto")
     ap.add_argument("--rotate", type=int, default=0, help="independent copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
@@ -269,15 +280,22 @@ def main():
     cfg = configs()[a.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    flags = {"auto": 0, "store": z.STORE_G, "recompute": z.RECOMPUTE_G}[a.design]
-    store_g = bool(flags & z.STORE_G) or (not (flags & z.RECOMPUTE_G) and cfg.W > 4)
+    flags = {"auto": 0, "onchip": z.ONCHIP, "store": z.STORE_G, "recompute": z.RECOMPUTE_G}[a.design]
+    store_g = bool(flags & z.STORE_G) or (not (flags & (z.RECOMPUTE_G | z.ONCHIP)) and cfg.W > 4)
     per_copy = cfg.S * (2 * cfg.W + 26 + (4 if store_g else 0))
     n_copies = a.rotate or (2 if per_copy < (1 << 30) else 1)
     st = setup(torch, cfg, flags, n_copies, dev)
     S, W = st["S"], st["W"]
+    c0 = st["copies"][0]
+    design = z.mta_design(c0.grads, c0.begin, c0.plan, flags)
+    if design == 0:
+        print(f"design {a.design} is not possible for {a.config}", file=sys.stderr)
+        return 2
+    flags = (flags & ~(z.ONCHIP | z.STORE_G | z.RECOMPUTE_G)) | design   # run the resolved design explicitly
+    design_name = {z.ONCHIP: "onchip", z.STORE_G: "store_g", z.RECOMPUTE_G: "recompute_g"}[design]
 
     if a.pmc_run:
-        run_steps(torch, z, cfg, st, flags, 0, 4)
+        run_steps(z, cfg, st, flags, 0, 4)
         x = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         y = torch.empty_like(x)
         torch.cuda.synchronize()
@@ -287,29 +305,36 @@ def main():
         print("pmc run done", flush=True)
         return 0
 
-    run_steps(torch, z, cfg, st, flags, 0, a.warmup)
+    run_steps(z, cfg, st, flags, 0, a.warmup)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    # the timed region: exactly K steps back to back, bracketed by synchronizations
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(torch, z, cfg, st, flags, a.warmup, a.warmup + a.steps, events)
+    g0.record()
+    run_steps(z, cfg, st, flags, a.warmup, a.warmup + a.steps)
+    g1.record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    red_ms = [e[0].elapsed_time(e[1]) for e in events]
-    upd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    gpu_ms_per_step = g0.elapsed_time(g1) / a.steps
+    # the dominant kernel's own duration: the same K steps again, each bracketed
+    # by HIP events on the stream the library launches on (torch's current stream)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    run_steps(z, cfg, st, flags, a.warmup + a.steps, a.warmup + 2 * a.steps, events)
+    torch.cuda.synchronize()
+    kern_ms = [e[0].elapsed_time(e[1]) for e in events]
     ms_per_step = el * 1e3 / a.steps
     value = S / (ms_per_step * 1e-3)
     bpp = cfg.bytes_per_param
-    upd_avg = sum(upd_ms) / len(upd_ms)
-    red_avg = sum(red_ms) / len(red_ms)
-    upd_bytes = (18 if cfg.mv_bf16 else 26) * S          # master/m/v read+write + bf16 param write
-    achieved = upd_bytes / (upd_avg * 1e-3) / 1e9
-    traffic = traffic_from_summary(PMC_SUMMARY) if a.config == "C2" and n_copies == 2 and a.design == "auto" else None
-    info = torch.zeros(4, dtype=torch.float64, device=dev)
-    c = st["copies"][0]
-    z.mta_update(c.grads, c.begin, c.plan, hp(cfg, 1), c.rsd, W, flags=flags, info_out=info, ws=c.ws)
-    torch.cuda.synchronize()
-    ni = info.cpu().numpy()
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
+    # algorithmic bytes per launch of the dominant kernel: the whole step
+    # (2W+26 B/param) for the single launch; master/m/v read+write and the
+    # bf16 write (26 B/param, 18 with bf16 m,v) for the two-phase update
+    kern_bytes = ((18 if cfg.mv_bf16 else 26) if two_phase else bpp) * S
+    kern_name = UPDATE_KERNEL if two_phase else ONCHIP_KERNEL
+    achieved = kern_bytes / (kern_avg * 1e-3) / 1e9
+    traffic = traffic_from_summary(PMC_SUMMARY, kern_name) if (a.config == "C2" and a.design == "auto") else None
     out = {
         "metric": "params updated/s and achieved HBM GB/s (% of peak) per fused ZeRO-1 step",
         "value": value,
@@ -326,17 +351,16 @@ def main():
         "config": {
             "workload": cfg.workload,
             "W": W, "rank": st["rank"], "shard_params": S, "pieces": st["pieces"],
-            "bytes_per_param": bpp, "design": "store_g" if store_g else "recompute_g",
+            "bytes_per_param": bpp, "design": design_name,
             "rotated_copies": n_copies, "m_v": "bf16" if cfg.mv_bf16 else "fp32",
-            "global_norm": float(ni[1]), "clipped": bool(ni[2:4].view("int32")[1]),
         },
         "algorithmic_GBps": value * bpp / 1e9,
         "pct_of_peak_hbm": 100.0 * value * bpp / 1e9 / PEAK_HBM_GBS,
-        "kernels_ms": {"reduce_phase(reduce+finalize)": red_avg, "update(adamw_mta)": upd_avg},
-        "roofline": {"bound": "hbm", "kernel": UPDATE_KERNEL, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": upd_bytes},
+        "gpu_ms_per_step": gpu_ms_per_step,
+        "kernel_ms": kern_avg,
+        "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": kern_bytes},
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, S, st["begin"])

@@ -76,9 +76,15 @@ typedef enum zero1_status {
 #define ZERO1_MV_BF16      0x2u  /* m and v are stored as bf16 (uint16_t)           */
 #define ZERO1_RECOMPUTE_G  0x4u  /* step: the update re-reads the W slices          */
 #define ZERO1_STORE_G      0x8u  /* step: the reduce stores fp32 g in the workspace
-                                    and the update reads it back.  Neither flag:
-                                    the library picks the design with fewer bytes
-                                    (STORE_G when W > 4).                            */
+                                    and the update reads it back                     */
+#define ZERO1_ONCHIP       0x10u /* zero1_mta_step only: one cooperative launch that
+                                    keeps g in registers across a grid barrier
+                                    (exactly 2W+26 bytes/param); EINVAL when the
+                                    shard does not fit in one co-resident grid.
+                                    Opt-in: on MI355X the cooperative launch and the
+                                    grid barrier cost more than the g round trip
+                                    they save.  No design flag: STORE_G when W > 4
+                                    (fewer bytes than re-reading), else RECOMPUTE_G. */
 
 /* AdamW and clipping hyper-parameters of one step (host struct). */
 typedef struct zero1_hparams {
@@ -223,12 +229,16 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads,
  *   zero1_mta_reduce it follows.  A multi-GPU caller exchanges the ranks'
  *   partials between the two calls (one double per rank: the only data the
  *   step needs from other ranks once the gradients are reduced).
- * zero1_mta_step: zero1_mta_reduce with sumsq_out = rank_sumsq + my_rank,
- *   then zero1_mta_update: the whole step (1-5) for rank my_rank when the
- *   other ranks' partials are already in rank_sumsq.
- *   flags: ZERO1_STORE_G / ZERO1_RECOMPUTE_G / ZERO1_SUM_ONLY (ZERO1_MV_BF16
- *   comes from the plan).  Results are bit-identical to zero1_shard_reduce +
- *   zero1_adamw_step on the same shard. */
+ * zero1_mta_step: the whole step (1-5) for rank my_rank when the other
+ *   ranks' partials are already in rank_sumsq; entry my_rank is overwritten
+ *   with this rank's partial.  Either one cooperative launch (ZERO1_ONCHIP,
+ *   on request) or zero1_mta_reduce with sumsq_out = rank_sumsq + my_rank
+ *   followed by zero1_mta_update.
+ *   flags: one of ZERO1_ONCHIP / ZERO1_STORE_G / ZERO1_RECOMPUTE_G, and
+ *   ZERO1_SUM_ONLY (ZERO1_MV_BF16 comes from the plan).
+ * Every design gives bit-identical master, m, v and params for the same
+ * clip coefficient; this rank's fp64 partial depends on the launch shape
+ * only in its last bits (different fixed summation trees). */
 size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces);
 zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces,
                             uint32_t flags, void* table, size_t table_bytes,
@@ -242,6 +252,11 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
                               const double* rank_sumsq, int n_ranks, uint32_t flags,
                               zero1_norm_info* info_out, void* ws, size_t ws_bytes,
                               void* stream);
+/* Which design zero1_mta_step would run for these arguments on the current
+ * device: ZERO1_ONCHIP, ZERO1_STORE_G or ZERO1_RECOMPUTE_G; 0 when the
+ * arguments are invalid or an explicitly requested design is impossible. */
+int zero1_mta_design(const uint16_t* const* grads, int W, int64_t begin,
+                     const zero1_plan* plan, uint32_t flags);
 zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
                             const zero1_plan* plan, const zero1_hparams* hp,
                             double* rank_sumsq, int n_ranks, int my_rank,

@@ -135,7 +135,7 @@ def test_mta_plan_rejects_bad_piece_lists():
 
 
 def test_mta_table_bytes():
-    p = [(8192 * 3 + 1, 0, FAKE, FAKE, FAKE, FAKE), (5, 8192 * 3 + 1, FAKE, FAKE, FAKE, FAKE)]
+    p = [(2048 * 3 + 1, 0, FAKE, FAKE, FAKE, FAKE), (5, 2048 * 3 + 1, FAKE, FAKE, FAKE, FAKE)]
     assert z.mta_table_bytes(p) == 256 + 16 * (4 + 1)
 
 

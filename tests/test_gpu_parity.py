@@ -190,6 +190,15 @@ def test_adamw_step_flat_parity(env, mv_bf16, source):
 
 # ---------------------------------------------------------------- multi-tensor apply
 RAGGED = [3000, 17, 5000, 8, 2203, 1, 65536 + 3, 768, 8192 * 2, 40000]
+# ragged against the 2048-element tiles but every piece 8-aligned, and a total
+# that every W in the tests cuts into 8-aligned shards: what the single-launch
+# (on-chip) design needs, and what real tensor lists look like
+RAGGED8 = [3000, 16, 5000, 8, 2208, 8, 65536 + 8, 768, 8192 * 2, 40120]
+assert sum(RAGGED8) % (8 * 24) == 0
+
+
+def ragged_for(design):
+    return RAGGED8 if design == z.ONCHIP else RAGGED
 
 
 def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_state, sigma_fn,
@@ -246,18 +255,18 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
 
 
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
+@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
 def test_mta_parity_ragged_all_ranks(env, W, design):
     torch, dev = env
-    run_mta_all_ranks(torch, dev, RAGGED, W, 3, 0xA000 + W, design, False, True,
+    run_mta_all_ranks(torch, dev, ragged_for(design), W, 3, 0xA000 + W, design, False, True,
                       lambda t: [0.02, 1e-4, 0.3][t % 3])
 
 
 @pytest.mark.parametrize("mv_bf16,flat_state", [(True, True), (False, False), (True, False)])
 def test_mta_parity_state_layouts(env, mv_bf16, flat_state):
     torch, dev = env
-    for design in (z.STORE_G, z.RECOMPUTE_G):
-        run_mta_all_ranks(torch, dev, RAGGED, 4, 3, 0xB000, design, mv_bf16, flat_state,
+    for design in (z.ONCHIP, z.STORE_G, z.RECOMPUTE_G):
+        run_mta_all_ranks(torch, dev, ragged_for(design), 4, 3, 0xB000, design, mv_bf16, flat_state,
                           lambda t: [0.02, 1e-4, 0.3][t % 3])
 
 
@@ -270,13 +279,31 @@ def test_mta_misaligned_pieces(env):
                       lambda t: 0.1)
 
 
-def test_c1_full_trajectory(env):
-    """C1: flat 2^20 parameters, W=4, every rank, 10 steps, against the oracle."""
+@pytest.mark.parametrize("design", [0, z.STORE_G, z.RECOMPUTE_G])
+def test_c1_full_trajectory(env, design):
+    """C1: flat 2^20 parameters, W=4, every rank, 10 steps, against the oracle
+    (design 0: the library's choice, the single-launch on-chip step)."""
     from synth.workloads import configs
     c = configs()["C1"]
     torch, dev = env
-    run_mta_all_ranks(torch, dev, [c.n_total], c.W, c.steps, c.seed, 0, False, True,
+    run_mta_all_ranks(torch, dev, [c.n_total], c.W, c.steps, c.seed, design, False, True,
                       lambda t: c.sigma)
+
+
+def test_onchip_rejects_what_does_not_fit(env):
+    torch, dev = env
+    master_full = synth.f32(20000, 1, 0, 0.02)
+    a = MtaShard(torch, dev, [13, 19987], 1, 0, master_full)      # misaligned second piece
+    ws = a.workspace(z.ONCHIP)
+    gd = [torch.zeros(20000, dtype=torch.int16, device=dev)]
+    rs = torch.zeros(1, dtype=torch.float64, device=dev)
+    with pytest.raises(z.Zero1Error) as e:
+        z.mta_step(gd, 0, a.plan, hp_at(1), rs, 1, 0, flags=z.ONCHIP, ws=ws)
+    assert "ONCHIP" in e.value.message
+    with pytest.raises(z.Zero1Error):
+        z.mta_reduce(gd, 0, a.plan, rs, flags=z.ONCHIP, ws=ws)
+    with pytest.raises(z.Zero1Error):
+        z.mta_step(gd, 0, a.plan, hp_at(1), rs, 1, 0, flags=z.ONCHIP | z.STORE_G, ws=ws)
 
 
 # ---------------------------------------------------------------- properties
@@ -309,6 +336,32 @@ def test_mta_equals_reduce_plus_adamw(env):
     assert_f32_equal(m, fmm.cpu().numpy(), "m")
     assert_f32_equal(v, fvv.cpu().numpy(), "v")
     assert_bf16_equal(param, to_np_u16(fp), "param")
+
+
+def test_onchip_equals_two_phase(env):
+    """The single-launch step and the two-kernel step give the same state bit
+    for bit (their fp64 partials may differ in the last bits only)."""
+    torch, dev = env
+    W, r = 8, 3
+    N = 8 * 23456            # 8-aligned shards; each ends in a partial 2048-element tile
+    master_full = synth.f32(N, synth.master_key(12), 0, 0.02)
+    a = MtaShard(torch, dev, [N], W, r, master_full)
+    b = MtaShard(torch, dev, [N], W, r, master_full)
+    wa, wb = a.workspace(z.ONCHIP), b.workspace(z.STORE_G)
+    for t in range(1, 5):
+        G = replicas(12, t, W, N, 0.3)
+        gd = [to_dev_u16(torch, x, dev) for x in G]
+        ra = torch.full((W,), 0.25, dtype=torch.float64, device=dev)
+        rb = ra.clone()
+        ia = torch.zeros(4, dtype=torch.float64, device=dev)
+        ib = torch.zeros(4, dtype=torch.float64, device=dev)
+        z.mta_step(gd, a.begin, a.plan, hp_at(t), ra, W, r, flags=z.ONCHIP, info_out=ia, ws=wa)
+        z.mta_step(gd, b.begin, b.plan, hp_at(t), rb, W, r, flags=z.STORE_G, info_out=ib, ws=wb)
+        torch.cuda.synchronize()
+        assert rel_close(ra[r].item(), rb[r].item(), NORM_TOL)
+        assert ia.cpu().numpy()[2:4].tobytes() == ib.cpu().numpy()[2:4].tobytes()   # coef, clip, flags
+    for x, y in zip(a.gather(), b.gather()):
+        assert x.tobytes() == y.tobytes()
 
 
 def test_rerun_is_bit_identical_and_resume_is_exact(env):

@@ -7,10 +7,10 @@ library is missing, importing the binding functions raises.
 """
 from .binding import (  # noqa: F401
     Zero1Error, HParams, NormInfo, Piece, Plan,
-    SUM_ONLY, MV_BF16, RECOMPUTE_G, STORE_G, MAX_W,
+    SUM_ONLY, MV_BF16, RECOMPUTE_G, STORE_G, ONCHIP, MAX_W,
     abi_version, last_error, shard_range, workspace_bytes,
     shard_reduce, grad_norm, adamw_step,
-    mta_table_bytes, mta_plan, mta_workspace_bytes, mta_reduce, mta_update, mta_step,
+    mta_table_bytes, mta_plan, mta_workspace_bytes, mta_reduce, mta_update, mta_design, mta_step,
     lib, lib_path,
 )
 from .layout import shard_pieces  # noqa: F401

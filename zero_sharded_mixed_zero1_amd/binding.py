@@ -11,12 +11,14 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(HERE, "libzero1.so")
+# ZERO1_LIB points the binding at another build of the same library (tuning)
+lib_path = os.environ.get("ZERO1_LIB") or os.path.join(HERE, "libzero1.so")
 
 SUM_ONLY = 0x1
 MV_BF16 = 0x2
 RECOMPUTE_G = 0x4
 STORE_G = 0x8
+ONCHIP = 0x10
 MAX_W = 128
 
 P = ctypes.c_void_p
@@ -96,6 +98,8 @@ def lib():
         L.zero1_mta_update.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                        P, i32, u32, P, P, szt, P]
         L.zero1_mta_update.restype = i32
+        L.zero1_mta_design.argtypes = [P, i32, i64, ctypes.POINTER(Plan), u32]
+        L.zero1_mta_design.restype = i32
         L.zero1_mta_step.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                      P, i32, i32, u32, P, P, szt, P]
         L.zero1_mta_step.restype = i32
@@ -247,6 +251,12 @@ def mta_update(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, flag
     _check(lib().zero1_mta_update(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
                                   ctypes.byref(h), _addr(rank_sumsq), n_ranks, flags,
                                   _addr(info_out), w, wb, _stream(stream)))
+
+
+def mta_design(grads, begin: int, plan: Plan, flags: int = 0) -> int:
+    """The design flag (ONCHIP, STORE_G or RECOMPUTE_G) mta_step would run; 0 if none."""
+    arr = _ptrs(grads)
+    return lib().zero1_mta_design(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan), flags)
 
 
 def mta_step(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, my_rank: int,

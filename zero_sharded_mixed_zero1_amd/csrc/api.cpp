@@ -131,16 +131,23 @@ zero1_status carve(void* ws, size_t bytes, size_t need, bool want_g, Ws& out)
 // CU several times over, never more than there are tiles.
 int grid_for(int64_t units, const DevInfo& d, int per_cu)
 {
-    int64_t cap = (int64_t)d.cus * per_cu;
+    int64_t cap = per_cu > 0 ? (int64_t)d.cus * per_cu : units;   // per_cu <= 0: one workgroup per unit
     if (cap > kMaxPartials) cap = kMaxPartials;
     int64_t n = units < cap ? units : cap;
     return (int)(n > 0 ? n : 1);
 }
 
-int64_t tiles(int64_t len, bool vec) { return (len + (int64_t)kThreads * (vec ? kVec : 1) - 1) / ((int64_t)kThreads * (vec ? kVec : 1)); }
+int64_t tiles(int64_t len, bool /*vec*/) { return (len + kTile - 1) / kTile; }
 
-constexpr int kReducePerCu = 8;
-constexpr int kAdamPerCu = 8;
+// Workgroups per CU of the persistent grids.  Defaults are the best measured
+// on MI355X; ZERO1_REDUCE_PER_CU / ZERO1_UPDATE_PER_CU override them (tuning).
+int env_int(const char* name, int dflt)
+{
+    const char* s = std::getenv(name);
+    return (s && *s) ? std::atoi(s) : dflt;
+}
+const int kReducePerCu = env_int("ZERO1_REDUCE_PER_CU", 8);
+const int kAdamPerCu = env_int("ZERO1_UPDATE_PER_CU", 0);   // 0: one workgroup per chunk/tile
 
 // ------------------------------------------------------------------ checks
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
@@ -363,12 +370,25 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
 }
 
 // ------------------------------------------------------------------ multi-tensor
+// Elements per multi-tensor chunk (a multiple of the 2048-element tile);
+// ZERO1_CHUNK_ELEMS overrides the default (tuning).
+static int64_t plan_chunk_elems()
+{
+    static const int64_t c = [] {
+        int64_t v = env_int("ZERO1_CHUNK_ELEMS", kChunkElems);
+        v = (v + kTile - 1) / kTile * kTile;
+        return v < kTile ? (int64_t)kTile : (v > (1 << 20) ? (int64_t)(1 << 20) : v);
+    }();
+    return c;
+}
+
 size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces)
 {
     if (!pieces || n_pieces <= 0) return 0;
+    const int64_t chunk = plan_chunk_elems();
     size_t chunks = 0;
     for (int i = 0; i < n_pieces; ++i)
-        if (pieces[i].numel > 0) chunks += (size_t)((pieces[i].numel + kChunkElems - 1) / kChunkElems);
+        if (pieces[i].numel > 0) chunks += (size_t)((pieces[i].numel + chunk - 1) / chunk);
     return round_up(sizeof(PieceDesc) * (size_t)n_pieces, 256) + sizeof(ChunkDesc) * chunks;
 }
 
@@ -422,6 +442,7 @@ zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t fl
     if ((st = current_device(d))) return st;
 
     const size_t chunk_off = round_up(sizeof(PieceDesc) * (size_t)n_pieces, 256);
+    const int64_t chunk = plan_chunk_elems();
     std::vector<char> host(need, 0);
     PieceDesc* pd = reinterpret_cast<PieceDesc*>(host.data());
     ChunkDesc* cd = reinterpret_cast<ChunkDesc*>(host.data() + chunk_off);
@@ -429,8 +450,8 @@ zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t fl
     for (int k = 0; k < n_pieces; ++k) {   // shard order, so chunk k covers shard positions in order
         const zero1_piece& p = pieces[order[k]];
         pd[k] = PieceDesc{p.numel, p.shard_offset, p.param_bf16, p.master, p.m, p.v};
-        for (int64_t off = 0; off < p.numel; off += kChunkElems) {
-            const int64_t l = std::min<int64_t>(kChunkElems, p.numel - off);
+        for (int64_t off = 0; off < p.numel; off += chunk) {
+            const int64_t l = std::min<int64_t>(chunk, p.numel - off);
             cd[nc++] = ChunkDesc{k, (int32_t)l, off};
         }
     }
@@ -440,7 +461,7 @@ zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t fl
     plan_out->shard_len = pos;
     plan_out->n_pieces = n_pieces;
     plan_out->n_chunks = (int32_t)nc;
-    plan_out->chunk_elems = kChunkElems;
+    plan_out->chunk_elems = (int32_t)chunk;
     plan_out->flags = flags & ZERO1_MV_BF16;
     plan_out->aligned = aligned ? 1 : 0;
     plan_out->reserved = 0;
@@ -449,9 +470,30 @@ zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t fl
 
 static bool use_store_g(uint32_t flags, int W)
 {
+    if (flags & ZERO1_ONCHIP) return false;
     if (flags & ZERO1_STORE_G) return true;
     if (flags & ZERO1_RECOMPUTE_G) return false;
     return W > 4;   // 2W+34 bytes/param beats 4W+26 once W > 4
+}
+
+// Single-launch design: the smallest K (tiles held per workgroup) whose
+// co-resident grid holds every chunk.  Returns K and the grid, or 0.
+static int pick_onchip(const zero1_plan* plan, const DevInfo& d, int& grid)
+{
+    if (plan->chunk_elems != kTile) return 0;
+    int ks[8];
+    const int n = onchip_variants(ks, 8);
+    for (int i = 0; i < n; ++i) {
+        int per_cu = 0;
+        if (onchip_max_blocks(ks[i], (plan->flags & ZERO1_MV_BF16) != 0, &per_cu) != hipSuccess || per_cu < 1)
+            continue;
+        int64_t cap = std::min<int64_t>((int64_t)per_cu * d.cus, kMaxPartials);
+        if ((int64_t)plan->n_chunks <= (int64_t)ks[i] * cap) {
+            grid = (int)std::min<int64_t>(cap, plan->n_chunks);
+            return ks[i];
+        }
+    }
+    return 0;
 }
 
 size_t zero1_mta_workspace_bytes(const zero1_plan* plan, int W, uint32_t flags)
@@ -467,8 +509,9 @@ static zero1_status mta_common(const uint16_t* const* grads, int W, int64_t begi
 {
     zero1_status st;
     if (!plan || !plan->table) return fail(ZERO1_EINVAL, "plan is NULL or has no table");
-    if ((flags & ZERO1_STORE_G) && (flags & ZERO1_RECOMPUTE_G))
-        return fail(ZERO1_EINVAL, "ZERO1_STORE_G and ZERO1_RECOMPUTE_G are exclusive");
+    const uint32_t designs = flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
+    if (designs & (designs - 1))
+        return fail(ZERO1_EINVAL, "ZERO1_STORE_G, ZERO1_RECOMPUTE_G and ZERO1_ONCHIP are exclusive");
     if ((st = check_grads(grads, W, begin, plan->shard_len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
     vec = vec && plan->aligned;
     store_g = use_store_g(flags, W);
@@ -484,6 +527,7 @@ zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin
     DevInfo d;
     Ws w;
     if (!sumsq_out) return fail(ZERO1_EINVAL, "sumsq_out is NULL");
+    if (flags & ZERO1_ONCHIP) return fail(ZERO1_EINVAL, "ZERO1_ONCHIP applies to zero1_mta_step only");
     zero1_status st = mta_common(grads, W, begin, plan, flags, ws, ws_bytes, r, vec, store_g, d, w);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -501,6 +545,7 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
     if ((st = check_hparams(hp))) return st;
     if (n_ranks < 1) return fail(ZERO1_EINVAL, "n_ranks=%d must be >= 1", n_ranks);
     if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
+    if (flags & ZERO1_ONCHIP) return fail(ZERO1_EINVAL, "ZERO1_ONCHIP applies to zero1_mta_step only");
     Reduce r;
     bool vec = false, store_g = false;
     DevInfo d;
@@ -516,6 +561,26 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
     return finish(s);
 }
 
+int zero1_mta_design(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan, uint32_t flags)
+{
+    if (!plan || !plan->table) return 0;
+    const uint32_t designs = flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
+    if (designs & (designs - 1)) return 0;
+    Reduce r;
+    bool vec = false;
+    if (check_grads(grads, W, begin, plan->shard_len, r, false, vec) != ZERO1_OK) return 0;
+    vec = vec && plan->aligned;
+    if (flags & ZERO1_STORE_G) return ZERO1_STORE_G;
+    if (flags & ZERO1_RECOMPUTE_G) return ZERO1_RECOMPUTE_G;
+    if (flags & ZERO1_ONCHIP) {
+        DevInfo d;
+        if (current_device(d) != ZERO1_OK) return 0;
+        int grid = 0;
+        return (vec && pick_onchip(plan, d, grid) > 0) ? (int)ZERO1_ONCHIP : 0;
+    }
+    return use_store_g(flags, W) ? ZERO1_STORE_G : ZERO1_RECOMPUTE_G;
+}
+
 zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
                             const zero1_hparams* hp, double* rank_sumsq, int n_ranks, int my_rank,
                             uint32_t flags, zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
@@ -525,6 +590,29 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
     if (n_ranks < 1 || my_rank < 0 || my_rank >= n_ranks)
         return fail(ZERO1_EINVAL, "my_rank=%d must be in [0, n_ranks=%d)", my_rank, n_ranks);
     if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
+    if (flags & ZERO1_ONCHIP) {
+        Reduce r;
+        bool vec = false, store_g = false;
+        DevInfo d;
+        Ws w;
+        if ((st = mta_common(grads, W, begin, plan, flags, ws, ws_bytes, r, vec, store_g, d, w))) return st;
+        int grid = 0;
+        const int k = vec ? pick_onchip(plan, d, grid) : 0;
+        if (k > 0) {
+            hipStream_t s = static_cast<hipStream_t>(stream);
+            const char* tb = static_cast<const char*>(plan->table);
+            const PieceDesc* pd = reinterpret_cast<const PieceDesc*>(tb);
+            const ChunkDesc* cd =
+                reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
+            Z1_HIP(launch_onchip(k, r, pd, cd, plan->n_chunks, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp),
+                                 w.partials, rank_sumsq, n_ranks, my_rank, hp->max_norm,
+                                 reinterpret_cast<NormInfo*>(info_out), grid, s));
+            return finish(s);
+        }
+        return fail(ZERO1_EINVAL, "ZERO1_ONCHIP: the shard (%lld elements, %d chunks) does not fit in one "
+                        "co-resident grid, or its buffers are not 16-byte aligned", (long long)plan->shard_len,
+                        plan->n_chunks);
+    }
     if ((st = zero1_mta_reduce(grads, W, begin, plan, rank_sumsq + my_rank, flags, ws, ws_bytes, stream))) return st;
     return zero1_mta_update(grads, W, begin, plan, hp, rank_sumsq, n_ranks, flags, info_out, ws, ws_bytes, stream);
 }

@@ -10,9 +10,10 @@ namespace z1 {
 
 constexpr int kMaxW = 128;          // == ZERO1_MAX_W
 constexpr int kThreads = 256;       // threads per workgroup (4 waves of 64)
-constexpr int kVec = 8;             // elements per thread per 16-byte bf16 access
+constexpr int kVec = 8;             // alignment unit (elements) of the vector path
+constexpr int kTile = 2048;         // elements per workgroup tile: 256 lanes x 8
 constexpr int kMaxPartials = 8192;  // capacity of the per-workgroup norm partials
-constexpr int kChunkElems = 8192;   // multi-tensor chunk: 256 threads x 8 elements x 4
+constexpr int kChunkElems = 2048;   // multi-tensor chunk: one tile
 
 // W gradient slice pointers, passed by value in the kernel arguments (1 KiB).
 struct GradPtrs {
@@ -86,5 +87,12 @@ hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pi
                             bool mv_bf16, const Scal& sc, const double* rank_sumsq,
                             int n_ranks, double max_norm, NormInfo* info_out,
                             int nblocks, hipStream_t s);
+// Single-launch step (cooperative grid barrier) for shards whose reduced
+// gradient fits in registers: K tiles per workgroup.
+int onchip_variants(int* ks, int max_n);
+hipError_t onchip_max_blocks(int k, bool mv_bf16, int* blocks_per_cu);
+hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks, int n_chunks,
+                         bool mv_bf16, const Scal& sc, double* partials, double* rank_sumsq, int n_ranks,
+                         int my_rank, double max_norm, NormInfo* info_out, int nblocks, hipStream_t s);
 
 }  // namespace z1

@@ -1,11 +1,22 @@
 // kernels.hip -- gfx950 kernels of one rank's ZeRO-1 optimizer step.
 //
 // Everything here is HBM-bound elementwise work (about 0.5 flop per byte), so
-// the design rules are those of a streaming kernel on CDNA4: 16-byte coalesced
-// accesses (8 bf16 or 4 fp32 per lane), enough workgroups per CU to keep loads
-// in flight, one pass over each array per phase, no atomics, no MFMA.
+// the rules are those of a streaming kernel on CDNA4:
+//   * Work is cut into tiles of 2048 elements per 256-lane workgroup.  Inside a
+//     tile, wave w owns elements [512w, 512w+512) and lane l of it the two
+//     quads [512w+4l, +4) and [512w+256+4l, +4), so every load or store
+//     instruction of a wave covers one contiguous run (512 B of bf16, 1 KiB of
+//     fp32): fully coalesced for both element sizes.
+//   * Every array is touched once per phase, so all accesses carry the
+//     non-temporal hint (global_load/store ... nt): streaming data should not
+//     displace anything in L2/MALL.  On MI355X this is worth ~1.5-2x over
+//     plain accesses for these kernels.
+//   * A persistent grid (a few workgroups per CU) walks the tiles with a
+//     grid stride; no atomics, no MFMA (nothing here is a contraction).
+//   * Tiles that run past the end, and shards whose pointers are not 16-byte
+//     aligned, take an element path (lane t handles t, t+256, ...).
 //
-// Arithmetic contract (matches the page's AdamW code on "并行训练", section
+// Arithmetic contract (the page's AdamW code on "并行训练", section
 // "一张卡上装了什么：混合精度与 AdamW", applied one binary32 operation at a time):
 // built with -ffp-contract=off and the pragma below, so no multiply-add is
 // fused; fp32 '/' and sqrtf are the correctly rounded HIP defaults; subnormals
@@ -13,9 +24,10 @@
 // fp64, so fma(x, x, acc) rounds exactly like acc + x*x).
 //
 // Determinism: every workgroup owns a fixed set of tiles, every lane adds its
-// own elements in index order, and partial sums are combined by a fixed tree
+// own elements in a fixed order, and partial sums are combined by a fixed tree
 // (wave butterfly, then the four waves in order), so a rerun with the same
 // launch shape reproduces every bit, including the norm.
+#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,6 +37,37 @@
 
 namespace z1 {
 namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- memory access
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
+
+// The reduced gradient g (store-g design) is written by one kernel and read
+// back by the next, so unlike every other array its accesses keep the default
+// cache policy: much of the re-read then hits the 256 MB MALL (measured on the
+// GPT-2 small W=8 shard: update kernel 82 -> 75 us).  Z1_G_TEMPORAL=0 gives g
+// the non-temporal hint too.
+#ifndef Z1_G_TEMPORAL
+#define Z1_G_TEMPORAL 1
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_g(const T* p)
+{
+    if constexpr (Z1_G_TEMPORAL) return *p; else return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void st_g(T* p, T v)
+{
+    if constexpr (Z1_G_TEMPORAL) *p = v; else __builtin_nontemporal_store(v, p);
+}
+
+// Offset of this lane's first quad inside a tile (the second is 256 further).
+__device__ __forceinline__ int quad_a() { return 512 * (int)(threadIdx.x >> 6) + 4 * (int)(threadIdx.x & 63); }
 
 // ------------------------------------------------------------- number formats
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -47,61 +90,98 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
 }
 
-// ------------------------------------------------------------- reduction
-// g[0..V) for V consecutive elements starting at e of every slice.
-// Accumulation order: s = G_0; s = s + G_w for w = 1..W-1; then the average.
-template <int V>
-__device__ __forceinline__ void reduce_group(const Reduce& r, int64_t e, float (&s)[V])
+// Eight values of this lane in a tile starting at p: quad a then quad b.
+__device__ __forceinline__ void ld8_bf16(const uint16_t* p, float (&x)[8])
 {
-    if constexpr (V == kVec) {
-        uint4 buf[8];
-        const uint4 a = *reinterpret_cast<const uint4*>(r.gp.p[0] + e);
-        s[0] = bf16_lo(a.x); s[1] = bf16_hi(a.x);
-        s[2] = bf16_lo(a.y); s[3] = bf16_hi(a.y);
-        s[4] = bf16_lo(a.z); s[5] = bf16_hi(a.z);
-        s[6] = bf16_lo(a.w); s[7] = bf16_hi(a.w);
-        for (int w0 = 1; w0 < r.W; w0 += 8) {
-            const int nb = r.W - w0 < 8 ? r.W - w0 : 8;
-            // issue up to eight 16-byte loads before the first dependent add
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (k < nb) buf[k] = *reinterpret_cast<const uint4*>(r.gp.p[w0 + k] + e);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                if (k < nb) {
-                    s[0] = s[0] + bf16_lo(buf[k].x); s[1] = s[1] + bf16_hi(buf[k].x);
-                    s[2] = s[2] + bf16_lo(buf[k].y); s[3] = s[3] + bf16_hi(buf[k].y);
-                    s[4] = s[4] + bf16_lo(buf[k].z); s[5] = s[5] + bf16_hi(buf[k].z);
-                    s[6] = s[6] + bf16_lo(buf[k].w); s[7] = s[7] + bf16_hi(buf[k].w);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-            float a = bf16_to_f32(r.gp.p[0][e + j]);
-            for (int w = 1; w < r.W; ++w)
-                a = a + bf16_to_f32(r.gp.p[w][e + j]);
-            s[j] = a;
-        }
-    }
-    if (r.mode == kAvgMulPow2) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) s[j] = s[j] * r.inv_w;
-    } else if (r.mode == kAvgDiv) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) s[j] = s[j] / r.f_w;
-    }
+    const int a = quad_a();
+    const u32x2 u = ld_nt(reinterpret_cast<const u32x2*>(p + a));
+    const u32x2 w = ld_nt(reinterpret_cast<const u32x2*>(p + a + 256));
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+    x[4] = bf16_lo(w.x); x[5] = bf16_hi(w.x); x[6] = bf16_lo(w.y); x[7] = bf16_hi(w.y);
 }
 
-__device__ __forceinline__ float reduce_one(const Reduce& r, int64_t e)
+__device__ __forceinline__ void st8_bf16(uint16_t* p, const float (&x)[8])
 {
-    float a = bf16_to_f32(r.gp.p[0][e]);
+    const int a = quad_a();
+    const u32x2 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    const u32x2 w = {pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    st_nt(reinterpret_cast<u32x2*>(p + a), u);
+    st_nt(reinterpret_cast<u32x2*>(p + a + 256), w);
+}
+
+__device__ __forceinline__ void ld8_f32(const float* p, float (&x)[8])
+{
+    const int a = quad_a();
+    const f32x4 u = ld_nt(reinterpret_cast<const f32x4*>(p + a));
+    const f32x4 w = ld_nt(reinterpret_cast<const f32x4*>(p + a + 256));
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+
+__device__ __forceinline__ void st8_g(float* p, const float (&x)[8])
+{
+    const int a = quad_a();
+    const f32x4 u = {x[0], x[1], x[2], x[3]};
+    const f32x4 w = {x[4], x[5], x[6], x[7]};
+    st_g(reinterpret_cast<f32x4*>(p + a), u);
+    st_g(reinterpret_cast<f32x4*>(p + a + 256), w);
+}
+
+__device__ __forceinline__ void ld8_g(const float* p, float (&x)[8])
+{
+    const int a = quad_a();
+    const f32x4 u = ld_g(reinterpret_cast<const f32x4*>(p + a));
+    const f32x4 w = ld_g(reinterpret_cast<const f32x4*>(p + a + 256));
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+}
+
+__device__ __forceinline__ void st8_f32(float* p, const float (&x)[8])
+{
+    const int a = quad_a();
+    const f32x4 u = {x[0], x[1], x[2], x[3]};
+    const f32x4 w = {x[4], x[5], x[6], x[7]};
+    st_nt(reinterpret_cast<f32x4*>(p + a), u);
+    st_nt(reinterpret_cast<f32x4*>(p + a + 256), w);
+}
+
+// ------------------------------------------------------------- reduction
+// Accumulation order for every element: s = G_0; s = s + G_w for w = 1..W-1;
+// then the average (multiply by the exact 2^-k, or an IEEE division).
+__device__ __forceinline__ float average(const Reduce& r, float s)
+{
+    if (r.mode == kAvgMulPow2) return s * r.inv_w;
+    if (r.mode == kAvgDiv) return s / r.f_w;
+    return s;
+}
+
+// This lane's 8 reduced values of the tile at shard index e (vector path).
+__device__ __forceinline__ void reduce8(const Reduce& r, int64_t e, float (&s)[8])
+{
+    ld8_bf16(r.gp.p[0] + e, s);
+    for (int w0 = 1; w0 < r.W; w0 += 4) {
+        // issue up to four slices' loads before the first dependent add
+        float x[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w0 + k < r.W) ld8_bf16(r.gp.p[w0 + k] + e, x[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (w0 + k < r.W) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s[j] = s[j] + x[k][j];
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = average(r, s[j]);
+}
+
+__device__ __forceinline__ float reduce1(const Reduce& r, int64_t e)
+{
+    float a = bf16_to_f32(ld_nt(r.gp.p[0] + e));
     for (int w = 1; w < r.W; ++w)
-        a = a + bf16_to_f32(r.gp.p[w][e]);
-    if (r.mode == kAvgMulPow2) a = a * r.inv_w;
-    else if (r.mode == kAvgDiv) a = a / r.f_w;
-    return a;
+        a = a + bf16_to_f32(ld_nt(r.gp.p[w] + e));
+    return average(r, a);
 }
 
 // ------------------------------------------------------------- block sum (fp64)
@@ -126,31 +206,26 @@ __device__ __forceinline__ double block_sum(double x)
 }
 
 // ------------------------------------------------------------- phase 1
-template <int V, bool STORE, bool NORM>
+template <bool VEC, bool STORE, bool NORM>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len, float* __restrict__ g_out,
                                                           double* __restrict__ partials)
 {
     double acc = 0.0;
-    const int64_t tile = (int64_t)kThreads * V;
-    const int64_t ntiles = (len + tile - 1) / tile;
+    const int64_t ntiles = (len + kTile - 1) / kTile;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t e = t * tile + (int64_t)threadIdx.x * V;
-        if (V > 1 && e + V <= len) {
-            float s[V];
-            reduce_group<V>(r, e, s);
-            if constexpr (STORE) {
-                float4* o = reinterpret_cast<float4*>(g_out + e);
-                o[0] = make_float4(s[0], s[1], s[2], s[3]);
-                o[1] = make_float4(s[4], s[5], s[6], s[7]);
-            }
+        const int64_t base = t * kTile;
+        if (VEC && base + kTile <= len) {
+            float s[8];
+            reduce8(r, base, s);
+            if constexpr (STORE) st8_g(g_out + base, s);
             if constexpr (NORM) {
 #pragma unroll
-                for (int j = 0; j < V; ++j) acc = fma((double)s[j], (double)s[j], acc);
+                for (int j = 0; j < 8; ++j) acc = fma((double)s[j], (double)s[j], acc);
             }
         } else {
-            for (int j = 0; j < V && e + j < len; ++j) {
-                const float x = reduce_one(r, e + j);
-                if constexpr (STORE) g_out[e + j] = x;
+            for (int64_t e = base + threadIdx.x; e < base + kTile && e < len; e += kThreads) {
+                const float x = reduce1(r, e);
+                if constexpr (STORE) st_g(g_out + e, x);
                 if constexpr (NORM) acc = fma((double)x, (double)x, acc);
             }
         }
@@ -161,24 +236,22 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len,
     }
 }
 
-template <int V>
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void sumsq_kernel(const float* __restrict__ g, int64_t len,
                                                          double* __restrict__ partials)
 {
     double acc = 0.0;
-    const int64_t tile = (int64_t)kThreads * V;
-    const int64_t ntiles = (len + tile - 1) / tile;
+    const int64_t ntiles = (len + kTile - 1) / kTile;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t e = t * tile + (int64_t)threadIdx.x * V;
-        if (V > 1 && e + V <= len) {
-            const float4* p = reinterpret_cast<const float4*>(g + e);
-            const float4 a = p[0], b = p[1];
-            const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const int64_t base = t * kTile;
+        if (VEC && base + kTile <= len) {
+            float s[8];
+            ld8_f32(g + base, s);
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc = fma((double)s[j], (double)s[j], acc);
         } else {
-            for (int j = 0; j < V && e + j < len; ++j) {
-                const double x = (double)g[e + j];
+            for (int64_t e = base + threadIdx.x; e < base + kTile && e < len; e += kThreads) {
+                const double x = (double)ld_nt(g + e);
                 acc = fma(x, x, acc);
             }
         }
@@ -195,7 +268,19 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const double* __rest
 {
     __shared__ double sh[kThreads];
     double a = 0.0;
-    for (int i = threadIdx.x; i < nb; i += kThreads) a = a + partials[i];
+    // the lane's strided subset in order; loads issued 8 at a time so that
+    // their latencies overlap (the adds stay in the same order)
+    for (int i0 = threadIdx.x; i0 < nb; i0 += 8 * kThreads) {
+        double x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = i0 + k * kThreads;
+            x[k] = i < nb ? partials[i] : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (i0 + k * kThreads < nb) a = a + x[k];
+    }
     sh[threadIdx.x] = a;
     __syncthreads();
     for (int s = kThreads / 2; s > 0; s >>= 1) {
@@ -264,122 +349,113 @@ __device__ __forceinline__ void adamw_elem(float g, float& p, float& m, float& v
     p = pn;
 }
 
-// Update n (<= V) consecutive elements.  gsrc: 0 = read g from `g` at shard
-// index gi, 1 = recompute g from the slices at shard index gi.  State index si.
-template <int V, int GSRC, bool MVBF16>
-__device__ __forceinline__ void step_group(const float* __restrict__ g, const Reduce& r, int64_t gi,
-                                           float* __restrict__ master, void* __restrict__ mp,
-                                           void* __restrict__ vp, uint16_t* __restrict__ param,
-                                           int64_t si, int n, const Scal& c, bool clip, float coef)
+// Where the update finds its arrays: g (fp32 buffer; unused when the gradient
+// is recomputed from the slices) and the state and param of one span.
+struct Span {
+    const float* g;
+    float* master;
+    void* m;
+    void* v;
+    uint16_t* param;
+};
+
+// The lane's 8 elements of a full tile at state index si, given their g.
+template <bool MVBF16>
+__device__ __forceinline__ void update8(const Span& sp, int64_t si, const float (&gv)[8], const Scal& c, bool clip,
+                                        float coef)
 {
-    if (V > 1 && n == V) {
-        float gv[8], p[8], m[8], v[8];
-        if constexpr (GSRC == 0) {
-            const float4* gp = reinterpret_cast<const float4*>(g + gi);
-            const float4 a = gp[0], b = gp[1];
-            gv[0] = a.x; gv[1] = a.y; gv[2] = a.z; gv[3] = a.w;
-            gv[4] = b.x; gv[5] = b.y; gv[6] = b.z; gv[7] = b.w;
-        } else {
-            reduce_group<8>(r, gi, gv);
-        }
-        const float4* pp = reinterpret_cast<const float4*>(master + si);
-        const float4 p0 = pp[0], p1 = pp[1];
-        p[0] = p0.x; p[1] = p0.y; p[2] = p0.z; p[3] = p0.w;
-        p[4] = p1.x; p[5] = p1.y; p[6] = p1.z; p[7] = p1.w;
-        if constexpr (MVBF16) {
-            const uint4 mb = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(mp) + si);
-            const uint4 vb = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(vp) + si);
-            m[0] = bf16_lo(mb.x); m[1] = bf16_hi(mb.x); m[2] = bf16_lo(mb.y); m[3] = bf16_hi(mb.y);
-            m[4] = bf16_lo(mb.z); m[5] = bf16_hi(mb.z); m[6] = bf16_lo(mb.w); m[7] = bf16_hi(mb.w);
-            v[0] = bf16_lo(vb.x); v[1] = bf16_hi(vb.x); v[2] = bf16_lo(vb.y); v[3] = bf16_hi(vb.y);
-            v[4] = bf16_lo(vb.z); v[5] = bf16_hi(vb.z); v[6] = bf16_lo(vb.w); v[7] = bf16_hi(vb.w);
-        } else {
-            const float4* mq = reinterpret_cast<const float4*>(static_cast<const float*>(mp) + si);
-            const float4* vq = reinterpret_cast<const float4*>(static_cast<const float*>(vp) + si);
-            const float4 m0 = mq[0], m1 = mq[1], v0 = vq[0], v1 = vq[1];
-            m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
-            m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
-            v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-            v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float gj = clip ? gv[j] * coef : gv[j];
-            adamw_elem(gj, p[j], m[j], v[j], c);
-        }
-        float4* po = reinterpret_cast<float4*>(master + si);
-        po[0] = make_float4(p[0], p[1], p[2], p[3]);
-        po[1] = make_float4(p[4], p[5], p[6], p[7]);
-        if constexpr (MVBF16) {
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(mp) + si) =
-                make_uint4(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]),
-                           pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7]));
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(vp) + si) =
-                make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-        } else {
-            float4* mo = reinterpret_cast<float4*>(static_cast<float*>(mp) + si);
-            float4* vo = reinterpret_cast<float4*>(static_cast<float*>(vp) + si);
-            mo[0] = make_float4(m[0], m[1], m[2], m[3]);
-            mo[1] = make_float4(m[4], m[5], m[6], m[7]);
-            vo[0] = make_float4(v[0], v[1], v[2], v[3]);
-            vo[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
-        *reinterpret_cast<uint4*>(param + si) =
-            make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    float p[8], m[8], v[8];
+    ld8_f32(sp.master + si, p);
+    if constexpr (MVBF16) {
+        ld8_bf16(static_cast<const uint16_t*>(sp.m) + si, m);
+        ld8_bf16(static_cast<const uint16_t*>(sp.v) + si, v);
     } else {
-        for (int j = 0; j < n; ++j) {
-            float gj = (GSRC == 0) ? g[gi + j] : reduce_one(r, gi + j);
-            if (clip) gj = gj * coef;
-            float p = master[si + j], m, v;
-            if constexpr (MVBF16) {
-                m = bf16_to_f32(static_cast<const uint16_t*>(mp)[si + j]);
-                v = bf16_to_f32(static_cast<const uint16_t*>(vp)[si + j]);
-            } else {
-                m = static_cast<const float*>(mp)[si + j];
-                v = static_cast<const float*>(vp)[si + j];
-            }
-            adamw_elem(gj, p, m, v, c);
-            master[si + j] = p;
-            if constexpr (MVBF16) {
-                static_cast<uint16_t*>(mp)[si + j] = (uint16_t)bf16_rne_bits(m);
-                static_cast<uint16_t*>(vp)[si + j] = (uint16_t)bf16_rne_bits(v);
-            } else {
-                static_cast<float*>(mp)[si + j] = m;
-                static_cast<float*>(vp)[si + j] = v;
-            }
-            param[si + j] = (uint16_t)bf16_rne_bits(p);
+        ld8_f32(static_cast<const float*>(sp.m) + si, m);
+        ld8_f32(static_cast<const float*>(sp.v) + si, v);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float gj = clip ? gv[j] * coef : gv[j];
+        adamw_elem(gj, p[j], m[j], v[j], c);
+    }
+    st8_f32(sp.master + si, p);
+    if constexpr (MVBF16) {
+        st8_bf16(static_cast<uint16_t*>(sp.m) + si, m);
+        st8_bf16(static_cast<uint16_t*>(sp.v) + si, v);
+    } else {
+        st8_f32(static_cast<float*>(sp.m) + si, m);
+        st8_f32(static_cast<float*>(sp.v) + si, v);
+    }
+    st8_bf16(sp.param + si, p);
+}
+
+// One element at state index si, given its g.
+template <bool MVBF16>
+__device__ __forceinline__ void update1(const Span& sp, int64_t si, float gj, const Scal& c, bool clip, float coef)
+{
+    if (clip) gj = gj * coef;
+    float p = ld_nt(sp.master + si), m, v;
+    if constexpr (MVBF16) {
+        m = bf16_to_f32(ld_nt(static_cast<const uint16_t*>(sp.m) + si));
+        v = bf16_to_f32(ld_nt(static_cast<const uint16_t*>(sp.v) + si));
+    } else {
+        m = ld_nt(static_cast<const float*>(sp.m) + si);
+        v = ld_nt(static_cast<const float*>(sp.v) + si);
+    }
+    adamw_elem(gj, p, m, v, c);
+    st_nt(sp.master + si, p);
+    if constexpr (MVBF16) {
+        st_nt(static_cast<uint16_t*>(sp.m) + si, (uint16_t)bf16_rne_bits(m));
+        st_nt(static_cast<uint16_t*>(sp.v) + si, (uint16_t)bf16_rne_bits(v));
+    } else {
+        st_nt(static_cast<float*>(sp.m) + si, m);
+        st_nt(static_cast<float*>(sp.v) + si, v);
+    }
+    st_nt(sp.param + si, (uint16_t)bf16_rne_bits(p));
+}
+
+// One tile [0, n) of a span (n <= kTile), g at shard index gi, state at si:
+// vector path when the whole tile is present (and VEC), element path otherwise.
+template <bool VEC, int GSRC, bool MVBF16>
+__device__ __forceinline__ void update_tile(const Span& sp, const Reduce& r, int64_t gi, int64_t si, int n,
+                                            const Scal& c, bool clip, float coef)
+{
+    if (VEC && n == kTile) {
+        float gv[8];
+        if constexpr (GSRC == 0) ld8_g(sp.g + gi, gv);
+        else reduce8(r, gi, gv);
+        update8<MVBF16>(sp, si, gv, c, clip, coef);
+    } else {
+        for (int j = threadIdx.x; j < n; j += kThreads) {
+            const float gj = (GSRC == 0) ? ld_g(sp.g + gi + j) : reduce1(r, gi + j);
+            update1<MVBF16>(sp, si + j, gj, c, clip, coef);
         }
     }
 }
 
-template <int V, int GSRC, bool MVBF16>
-__global__ __launch_bounds__(kThreads) void adamw_flat_kernel(const float* __restrict__ g, Reduce r,
-                                                              int64_t len, float* __restrict__ master,
-                                                              void* __restrict__ m, void* __restrict__ v,
-                                                              uint16_t* __restrict__ param, Scal c,
+template <bool VEC, int GSRC, bool MVBF16>
+__global__ __launch_bounds__(kThreads) void adamw_flat_kernel(Span sp, Reduce r, int64_t len, Scal c,
                                                               ClipArgs ca)
 {
     bool clip;
     float coef;
     block_clip(ca, clip, coef);
-    const int64_t tile = (int64_t)kThreads * V;
-    const int64_t ntiles = (len + tile - 1) / tile;
+    const int64_t ntiles = (len + kTile - 1) / kTile;
     for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int64_t e = t * tile + (int64_t)threadIdx.x * V;
-        if (e >= len) continue;
-        const int n = (int)(len - e < V ? len - e : V);
-        step_group<V, GSRC, MVBF16>(g, r, e, master, m, v, param, e, n, c, clip, coef);
+        const int64_t base = t * kTile;
+        const int n = (int)(len - base < kTile ? len - base : kTile);
+        update_tile<VEC, GSRC, MVBF16>(sp, r, base, base, n, c, clip, coef);
     }
 }
 
-template <int V, int GSRC, bool MVBF16>
+template <bool MVBF16>
+__device__ __forceinline__ Span chunk_span(const PieceDesc& pc, const ChunkDesc& ch);
+
+template <bool VEC, int GSRC, bool MVBF16>
 __global__ __launch_bounds__(kThreads) void adamw_mta_kernel(const float* __restrict__ g, Reduce r,
                                                              const PieceDesc* __restrict__ pieces,
                                                              const ChunkDesc* __restrict__ chunks,
-                                                             int n_chunks, Scal c,
-                                                             ClipArgs ca)
+                                                             int n_chunks, Scal c, ClipArgs ca)
 {
     bool clip;
     float coef;
@@ -387,16 +463,134 @@ __global__ __launch_bounds__(kThreads) void adamw_mta_kernel(const float* __rest
     for (int k = blockIdx.x; k < n_chunks; k += gridDim.x) {
         const ChunkDesc ch = chunks[k];
         const PieceDesc pc = pieces[ch.piece];
+        Span sp = chunk_span<MVBF16>(pc, ch);
+        sp.g = g;
         const int64_t g0 = pc.shard_offset + ch.offset;
-        float* master = pc.master + ch.offset;
-        void* m = MVBF16 ? (void*)(static_cast<uint16_t*>(pc.m) + ch.offset)
-                         : (void*)(static_cast<float*>(pc.m) + ch.offset);
-        void* v = MVBF16 ? (void*)(static_cast<uint16_t*>(pc.v) + ch.offset)
-                         : (void*)(static_cast<float*>(pc.v) + ch.offset);
-        uint16_t* param = pc.param + ch.offset;
-        for (int e = threadIdx.x * V; e < ch.len; e += kThreads * V) {
-            const int n = ch.len - e < V ? ch.len - e : V;
-            step_group<V, GSRC, MVBF16>(g, r, g0 + e, master, m, v, param, e, n, c, clip, coef);
+        for (int sub = 0; sub < ch.len; sub += kTile) {
+            const int n = ch.len - sub < kTile ? ch.len - sub : kTile;
+            update_tile<VEC, GSRC, MVBF16>(sp, r, g0 + sub, sub, n, c, clip, coef);
+        }
+    }
+}
+
+// ------------------------------------------------------------- single launch
+// The whole step in one cooperative launch for shards whose reduced gradient
+// fits in the register file: every workgroup reduces up to K one-tile chunks
+// and keeps their g in registers (8 per lane per chunk), publishes its fp64
+// partial, waits at a grid barrier, forms this rank's sum of squares from all
+// partials (every workgroup in the same fixed order), the global norm and the
+// clip decision, and then updates the same chunks from the registers.  The
+// reduced gradient never touches HBM: traffic is exactly 2W+26 bytes/param.
+struct OnchipArgs {
+    double* partials;       // gridDim.x entries
+    double* rank_sumsq;     // n_ranks entries; entry my_rank is written
+    int n_ranks;
+    int my_rank;
+    double max_norm;
+    NormInfo* info_out;     // may be null
+};
+
+// Span of one chunk's piece, starting at the chunk.
+template <bool MVBF16>
+__device__ __forceinline__ Span chunk_span(const PieceDesc& pc, const ChunkDesc& ch)
+{
+    const size_t mvb = MVBF16 ? 2 : 4;
+    Span sp;
+    sp.g = nullptr;
+    sp.master = pc.master + ch.offset;
+    sp.m = static_cast<char*>(pc.m) + mvb * ch.offset;
+    sp.v = static_cast<char*>(pc.v) + mvb * ch.offset;
+    sp.param = pc.param + ch.offset;
+    return sp;
+}
+
+template <int K, int MINW, bool MVBF16>
+__global__ __launch_bounds__(kThreads, MINW) void onchip_step_kernel(Reduce r, const PieceDesc* __restrict__ pieces,
+                                                                      const ChunkDesc* __restrict__ chunks,
+                                                                      int n_chunks, Scal c, OnchipArgs oa)
+{
+    float greg[K][8];
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int ci = blockIdx.x + k * gridDim.x;
+        if (ci < n_chunks) {
+            const ChunkDesc ch = chunks[ci];
+            const int64_t g0 = pieces[ch.piece].shard_offset + ch.offset;
+            if (ch.len == kTile) {
+                reduce8(r, g0, greg[k]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc = fma((double)greg[k][j], (double)greg[k][j], acc);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int j = threadIdx.x + kThreads * i;
+                    greg[k][i] = 0.0f;
+                    if (j < ch.len) {
+                        greg[k][i] = reduce1(r, g0 + j);
+                        acc = fma((double)greg[k][i], (double)greg[k][i], acc);
+                    }
+                }
+            }
+        }
+    }
+    const double b = block_sum(acc);
+    if (threadIdx.x == 0) oa.partials[blockIdx.x] = b;
+
+    cooperative_groups::this_grid().sync();
+
+    // this rank's sum of squares: the partials in the fixed order of finalize_kernel
+    __shared__ double sh[kThreads];
+    __shared__ NormInfo shi;
+    double a = 0.0;
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) a = a + oa.partials[i];
+    sh[threadIdx.x] = a;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double q_r = sh[0];
+        NormInfo ni;
+        double tot = 0.0;
+        for (int q = 0; q < oa.n_ranks; ++q) tot = tot + (q == oa.my_rank ? q_r : oa.rank_sumsq[q]);
+        ni.sumsq_total = tot;
+        ni.norm = sqrt(tot);
+        if (ni.norm > oa.max_norm) {
+            ni.clip = 1;
+            ni.clip_coef = (float)(oa.max_norm / ni.norm);
+        } else {
+            ni.clip = 0;
+            ni.clip_coef = 1.0f;
+        }
+        ni.nonfinite = (isnan(ni.norm) || isinf(ni.norm)) ? 1 : 0;
+        ni.reserved = 0;
+        shi = ni;
+        if (blockIdx.x == 0) {
+            oa.rank_sumsq[oa.my_rank] = q_r;     // no workgroup reads this entry
+            if (oa.info_out) *oa.info_out = ni;
+        }
+    }
+    __syncthreads();
+    const bool clip = shi.clip != 0;
+    const float coef = shi.clip_coef;
+
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int ci = blockIdx.x + k * gridDim.x;
+        if (ci < n_chunks) {
+            const ChunkDesc ch = chunks[ci];
+            const Span sp = chunk_span<MVBF16>(pieces[ch.piece], ch);
+            if (ch.len == kTile) {
+                update8<MVBF16>(sp, 0, greg[k], c, clip, coef);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int j = threadIdx.x + kThreads * i;
+                    if (j < ch.len) update1<MVBF16>(sp, j, greg[k][i], c, clip, coef);
+                }
+            }
         }
     }
 }
@@ -411,13 +605,13 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, d
     const bool store = g_out != nullptr, norm = partials != nullptr;
 #define Z1_REDUCE(V, ST, NO) hipLaunchKernelGGL((reduce_kernel<V, ST, NO>), grid, block, 0, s, r, len, g_out, partials)
     if (vec) {
-        if (store && norm) Z1_REDUCE(kVec, true, true);
-        else if (store) Z1_REDUCE(kVec, true, false);
-        else Z1_REDUCE(kVec, false, true);
+        if (store && norm) Z1_REDUCE(true, true, true);
+        else if (store) Z1_REDUCE(true, true, false);
+        else Z1_REDUCE(true, false, true);
     } else {
-        if (store && norm) Z1_REDUCE(1, true, true);
-        else if (store) Z1_REDUCE(1, true, false);
-        else Z1_REDUCE(1, false, true);
+        if (store && norm) Z1_REDUCE(false, true, true);
+        else if (store) Z1_REDUCE(false, true, false);
+        else Z1_REDUCE(false, false, true);
     }
 #undef Z1_REDUCE
     return hipGetLastError();
@@ -426,9 +620,9 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, d
 hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials, int nblocks, hipStream_t s)
 {
     if (vec)
-        hipLaunchKernelGGL((sumsq_kernel<kVec>), dim3(nblocks), dim3(kThreads), 0, s, g, len, partials);
+        hipLaunchKernelGGL((sumsq_kernel<true>), dim3(nblocks), dim3(kThreads), 0, s, g, len, partials);
     else
-        hipLaunchKernelGGL((sumsq_kernel<1>), dim3(nblocks), dim3(kThreads), 0, s, g, len, partials);
+        hipLaunchKernelGGL((sumsq_kernel<false>), dim3(nblocks), dim3(kThreads), 0, s, g, len, partials);
     return hipGetLastError();
 }
 
@@ -445,14 +639,15 @@ hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool 
 {
     const dim3 grid(nblocks), block(kThreads);
     const ClipArgs ca{rank_sumsq, n_ranks, max_norm, info_out};
-#define Z1_FLAT(V, GS, MV) hipLaunchKernelGGL((adamw_flat_kernel<V, GS, MV>), grid, block, 0, s, g, r, len, master, m, v, param, sc, ca)
+    const Span sp{g, master, m, v, param};
+#define Z1_FLAT(V, GS, MV) hipLaunchKernelGGL((adamw_flat_kernel<V, GS, MV>), grid, block, 0, s, sp, r, len, sc, ca)
     const int gs = g ? 0 : 1;
     if (vec) {
-        if (gs == 0) { if (mv_bf16) Z1_FLAT(kVec, 0, true); else Z1_FLAT(kVec, 0, false); }
-        else         { if (mv_bf16) Z1_FLAT(kVec, 1, true); else Z1_FLAT(kVec, 1, false); }
+        if (gs == 0) { if (mv_bf16) Z1_FLAT(true, 0, true); else Z1_FLAT(true, 0, false); }
+        else         { if (mv_bf16) Z1_FLAT(true, 1, true); else Z1_FLAT(true, 1, false); }
     } else {
-        if (gs == 0) { if (mv_bf16) Z1_FLAT(1, 0, true); else Z1_FLAT(1, 0, false); }
-        else         { if (mv_bf16) Z1_FLAT(1, 1, true); else Z1_FLAT(1, 1, false); }
+        if (gs == 0) { if (mv_bf16) Z1_FLAT(false, 0, true); else Z1_FLAT(false, 0, false); }
+        else         { if (mv_bf16) Z1_FLAT(false, 1, true); else Z1_FLAT(false, 1, false); }
     }
 #undef Z1_FLAT
     return hipGetLastError();
@@ -467,14 +662,58 @@ hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pi
 #define Z1_MTA(V, GS, MV) hipLaunchKernelGGL((adamw_mta_kernel<V, GS, MV>), grid, block, 0, s, g, r, pieces, chunks, n_chunks, sc, ca)
     const int gs = g ? 0 : 1;
     if (vec) {
-        if (gs == 0) { if (mv_bf16) Z1_MTA(kVec, 0, true); else Z1_MTA(kVec, 0, false); }
-        else         { if (mv_bf16) Z1_MTA(kVec, 1, true); else Z1_MTA(kVec, 1, false); }
+        if (gs == 0) { if (mv_bf16) Z1_MTA(true, 0, true); else Z1_MTA(true, 0, false); }
+        else         { if (mv_bf16) Z1_MTA(true, 1, true); else Z1_MTA(true, 1, false); }
     } else {
-        if (gs == 0) { if (mv_bf16) Z1_MTA(1, 0, true); else Z1_MTA(1, 0, false); }
-        else         { if (mv_bf16) Z1_MTA(1, 1, true); else Z1_MTA(1, 1, false); }
+        if (gs == 0) { if (mv_bf16) Z1_MTA(false, 0, true); else Z1_MTA(false, 0, false); }
+        else         { if (mv_bf16) Z1_MTA(false, 1, true); else Z1_MTA(false, 1, false); }
     }
 #undef Z1_MTA
     return hipGetLastError();
+}
+
+// K tiles held per workgroup and the minimum waves per SIMD the register
+// budget is sized for (K=8: 64 registers of g per lane, 4 waves/SIMD).
+#define Z1_ONCHIP_VARIANTS(X) X(2, 8) X(4, 5) X(8, 4) X(12, 3)
+
+static const void* onchip_fn(int k, bool mv_bf16)
+{
+#define Z1_FN(K, MW) if (k == K) return mv_bf16 ? (const void*)onchip_step_kernel<K, MW, true> : (const void*)onchip_step_kernel<K, MW, false>;
+    Z1_ONCHIP_VARIANTS(Z1_FN)
+#undef Z1_FN
+    return nullptr;
+}
+
+int onchip_variants(int* ks, int max_n)
+{
+    int n = 0;
+#define Z1_K(K, MW) if (n < max_n) ks[n++] = K;
+    Z1_ONCHIP_VARIANTS(Z1_K)
+#undef Z1_K
+    return n;
+}
+
+hipError_t onchip_max_blocks(int k, bool mv_bf16, int* blocks_per_cu)
+{
+    const void* f = onchip_fn(k, mv_bf16);
+    if (!f) return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+}
+
+hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks, int n_chunks,
+                         bool mv_bf16, const Scal& sc, double* partials, double* rank_sumsq, int n_ranks, int my_rank,
+                         double max_norm, NormInfo* info_out, int nblocks, hipStream_t s)
+{
+    const void* f = onchip_fn(k, mv_bf16);
+    if (!f) return hipErrorInvalidValue;
+    Reduce rr = r;
+    const PieceDesc* pd = pieces;
+    const ChunkDesc* cd = chunks;
+    int nc = n_chunks;
+    Scal cc = sc;
+    OnchipArgs oa{partials, rank_sumsq, n_ranks, my_rank, max_norm, info_out};
+    void* args[] = {&rr, &pd, &cd, &nc, &cc, &oa};
+    return hipLaunchCooperativeKernel(f, dim3(nblocks), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace z1
