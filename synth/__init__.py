@@ -70,6 +70,10 @@ def cpu_lib():
         L.synth_fill_f32.restype = None
         L.synth_fill_bf16.argtypes = [P, i64, u64, u64, f32, i32]
         L.synth_fill_bf16.restype = None
+        L.synth_gather_f32.argtypes = [P, P, i64, u64, f32, i32]
+        L.synth_gather_f32.restype = None
+        L.synth_gather_bf16.argtypes = [P, P, i64, u64, f32, i32]
+        L.synth_gather_bf16.restype = None
         _cpu = L
     return _cpu
 
@@ -112,6 +116,22 @@ def f32(n: int, k: int, i0: int, sigma: float, outlier_pct: int = 0) -> np.ndarr
 def bf16(n: int, k: int, i0: int, sigma: float, outlier_pct: int = 0) -> np.ndarray:
     out = np.empty(n, dtype=np.uint16)
     cpu_lib().synth_fill_bf16(out.ctypes.data, n, k, i0, sigma, outlier_pct)
+    return out
+
+
+def f32_at(idx: np.ndarray, k: int, sigma: float, outlier_pct: int = 0) -> np.ndarray:
+    """f32 draws at the given global indices."""
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(idx.size, dtype=np.float32)
+    cpu_lib().synth_gather_f32(out.ctypes.data, idx.ctypes.data, idx.size, k, sigma, outlier_pct)
+    return out
+
+
+def bf16_at(idx: np.ndarray, k: int, sigma: float, outlier_pct: int = 0) -> np.ndarray:
+    """bf16 draws at the given global indices."""
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(idx.size, dtype=np.uint16)
+    cpu_lib().synth_gather_bf16(out.ctypes.data, idx.ctypes.data, idx.size, k, sigma, outlier_pct)
     return out
 
 

@@ -72,3 +72,22 @@ void synth_fill_bf16(uint16_t* out, int64_t n, uint64_t key, uint64_t i0, float 
         out[j] = (uint16_t)(u >> 16);
     }
 }
+
+/* Draws at arbitrary global indices (for sampled checks of huge shards). */
+void synth_gather_f32(float* out, const int64_t* idx, int64_t n, uint64_t key, float sigma, int outlier_pct)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+        out[j] = synth_value(key, (uint64_t)idx[j], sigma, outlier_pct);
+}
+
+void synth_gather_bf16(uint16_t* out, const int64_t* idx, int64_t n, uint64_t key, float sigma, int outlier_pct)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        float x = synth_value(key, (uint64_t)idx[j], sigma, outlier_pct);
+        uint32_t u;
+        memcpy(&u, &x, sizeof u);
+        out[j] = (uint16_t)(u >> 16);
+    }
+}
