@@ -66,11 +66,13 @@ struct ChunkDesc {
 // ---- launchers (kernels.hip); each returns hipGetLastError() after launch.
 // Phase 1: g = reduce(slices) over [0, len); optional fp32 store of g and one
 // fp64 partial sum of squares per workgroup (nblocks of them).
+// `split`: 8 splits the units into one contiguous part per XCD, 1 is a plain
+// grid stride (nblocks must be a multiple of split).
 hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out,
-                         double* partials, int nblocks, hipStream_t s);
+                         double* partials, int nblocks, int split, hipStream_t s);
 // Sum of squares of an fp32 vector, one partial per workgroup.
 hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials,
-                        int nblocks, hipStream_t s);
+                        int nblocks, int split, hipStream_t s);
 // One workgroup: add the per-workgroup partials in a fixed order into *q_out.
 hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, hipStream_t s);
 // Phase 2 over a flat shard.  g == nullptr: recompute g from r.  Every
@@ -80,13 +82,13 @@ hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool 
                              bool mv_bf16, float* master, void* m, void* v,
                              uint16_t* param, const Scal& sc, const double* rank_sumsq,
                              int n_ranks, double max_norm, NormInfo* info_out,
-                             int nblocks, hipStream_t s);
+                             int nblocks, int split, hipStream_t s);
 // Phase 2 over a multi-tensor plan (same prologue).
 hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces,
                             const ChunkDesc* chunks, int n_chunks, bool vec,
                             bool mv_bf16, const Scal& sc, const double* rank_sumsq,
                             int n_ranks, double max_norm, NormInfo* info_out,
-                            int nblocks, hipStream_t s);
+                            int nblocks, int split, hipStream_t s);
 // Single-launch step (cooperative grid barrier) for shards whose reduced
 // gradient fits in registers: K tiles per workgroup.
 int onchip_variants(int* ks, int max_n);
