@@ -149,7 +149,7 @@ def run_steps(z, cfg, st, flags, k0, k1, events=None):
 
 
 # ---------------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, S_total, begin, budget_s=12.0):
+def cpu_baseline(cfg, S_total, begin, budget_s=12.0, max_steps=2000):
     """The oracle, as it stands, on the same rank's shard (a bounded sample):
     as many full steps as fit in about budget_s seconds of host time."""
     import numpy as np
@@ -171,7 +171,7 @@ def cpu_baseline(cfg, S_total, begin, budget_s=12.0):
         oracle.step(grads, master, m, v, param, hp(cfg, steps + 1), rs, cfg.rank % W)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 200:
+        if el >= budget_s or steps >= max_steps:
             break
     return {"value": n * steps / el, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} full oracle steps (reduce, norm, clip, AdamW, bf16) on the first {n:,} "
