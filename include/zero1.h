@@ -49,6 +49,9 @@
  *     rounded once to fp32.
  *   - Calls that share a workspace must not overlap in time (same stream, or
  *     ordered by the caller).
+ *   - Unknown flag bits are rejected (EINVAL); flags that do not concern an
+ *     entry point are ignored by it, so one flag set can be passed to every
+ *     call of a step.
  */
 #ifndef ZERO1_H
 #define ZERO1_H
@@ -85,6 +88,20 @@ typedef enum zero1_status {
                                     grid barrier cost more than the g round trip
                                     they save.  No design flag: STORE_G when W > 4
                                     (fewer bytes than re-reading), else RECOMPUTE_G. */
+
+/* Compatibility variants (not the pages' step; off by default):
+ *   ZERO1_DECAY_FIRST  decay the master before the Adam update, the order
+ *                      "并行训练" ("一张卡上装了什么：混合精度与 AdamW") attributes to
+ *                      torch.optim.AdamW (differs by ~lr^2*lambda per step);
+ *   ZERO1_CLIP_EPS     torch.nn.utils.clip_grad_norm_'s convention: coefficient
+ *                      max_norm / (norm + 1e-6), applied when it is below 1;
+ *   ZERO1_G_BF16       the reduced gradient is rounded to the nearest bf16
+ *                      before the norm and the update (what a reduce-scatter
+ *                      delivering bf16 hands to the optimizer); applies where
+ *                      the library forms g (a g passed in is used as is). */
+#define ZERO1_DECAY_FIRST  0x20u
+#define ZERO1_CLIP_EPS     0x40u
+#define ZERO1_G_BF16       0x80u
 
 /* AdamW and clipping hyper-parameters of one step (host struct). */
 typedef struct zero1_hparams {
@@ -157,7 +174,8 @@ size_t zero1_workspace_bytes(int64_t len, int W, uint32_t flags);
  *             gradient (bf16), indexed by flat position.
  *   W         1..ZERO1_MAX_W replicas.
  *   begin,len the shard [begin, begin+len) of the flat vector.
- *   flags     ZERO1_SUM_ONLY: output the sum instead of the average.
+ *   flags     ZERO1_SUM_ONLY: output the sum instead of the average;
+ *             ZERO1_G_BF16: round g to bf16 (compatibility variant).
  *   g_out     len fp32 outputs g[k] for flat element begin+k, or NULL.
  *             Must not overlap any gradient range.
  *   sumsq_out one double: sum of g[k]^2 over the shard (fp64, fixed order,
@@ -191,7 +209,8 @@ zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out,
  *   hp          (host) hyper-parameters; hp->step is t.
  *   rank_sumsq  n_ranks doubles: every rank's partial sum of squares (this
  *               rank's included), added in rank order for the global norm.
- *   flags       ZERO1_MV_BF16, ZERO1_SUM_ONLY (with g == NULL).
+ *   flags       ZERO1_MV_BF16; ZERO1_SUM_ONLY and ZERO1_G_BF16 (with g == NULL);
+ *               ZERO1_DECAY_FIRST, ZERO1_CLIP_EPS (compatibility variants).
  *   info_out    one zero1_norm_info (device) or NULL; written even when len == 0.
  * Needs no workspace: every workgroup forms the norm from rank_sumsq itself.
  * Per element, with c the clip coefficient when clipping:

@@ -82,6 +82,12 @@ def lib():
                                   f64, f64, f64, f64, f64, f64, i64,
                                   P, i32, i32, P, P]
         L.oracle_step.restype = i32
+        L.oracle_step_v.argtypes = L.oracle_step.argtypes + [ctypes.c_uint]
+        L.oracle_step_v.restype = i32
+        L.oracle_clip_coef_eps.argtypes = [f64, f64, ctypes.POINTER(f32)]
+        L.oracle_clip_coef_eps.restype = i32
+        L.oracle_round_to_bf16.argtypes = [P, i64]
+        L.oracle_round_to_bf16.restype = None
         L.oracle_zero_bytes_per_gpu.argtypes = [f64, f64, f64, i32]
         L.oracle_zero_bytes_per_gpu.restype = f64
         _lib = L
@@ -150,6 +156,20 @@ def clip_coef(norm: float, max_norm: float):
     return bool(flag), np.float32(c.value)
 
 
+def clip_coef_eps(norm: float, max_norm: float):
+    """Torch-convention clip (oracle_clip_coef_eps): returns (clip_flag, fp32 coefficient)."""
+    c = ctypes.c_float()
+    flag = lib().oracle_clip_coef_eps(float(norm), float(max_norm), ctypes.byref(c))
+    return bool(flag), np.float32(c.value)
+
+
+def round_to_bf16(g: np.ndarray) -> np.ndarray:
+    """Copy of g rounded to bf16 and widened (oracle_round_to_bf16)."""
+    out = np.ascontiguousarray(g, dtype=np.float32).copy()
+    lib().oracle_round_to_bf16(_ptr(out), out.size)
+    return out
+
+
 def adamw_scalars(lr, beta1, beta2, eps, weight_decay, t) -> Scalars:
     """O4 (oracle_adamw_scalars)."""
     s = Scalars()
@@ -187,13 +207,19 @@ class StepInfo:
         self.sumsq = float(info[3])
 
 
-def step(grads, master, m, v, param_bf16, hp, rank_sumsq, my_rank, average=True) -> StepInfo:
+DECAY_FIRST = 1
+CLIP_EPS = 2
+G_BF16 = 4
+
+
+def step(grads, master, m, v, param_bf16, hp, rank_sumsq, my_rank, average=True, variant=0) -> StepInfo:
     """One rank's whole step on a flat shard (oracle_step), in place.
 
     grads: list of W uint16 arrays (this rank's slice of each replica);
     master fp32; m, v fp32 or uint16 (bf16 moments); param_bf16 uint16;
     hp: dict with lr, beta1, beta2, eps, weight_decay, max_norm, step;
     rank_sumsq: float64 array of all ranks' partials (entry my_rank is written).
+    variant: DECAY_FIRST | CLIP_EPS | G_BF16 compatibility variants (0: the pages' step).
     """
     grads = [np.ascontiguousarray(g, dtype=np.uint16) for g in grads]
     n = master.size
@@ -203,11 +229,11 @@ def step(grads, master, m, v, param_bf16, hp, rank_sumsq, my_rank, average=True)
     scratch = np.empty(n, dtype=np.float32)
     info = np.zeros(4, dtype=np.float64)
     keep = _ptr_array(grads)
-    rc = lib().oracle_step(ctypes.cast(keep, ctypes.c_void_p), len(grads), n, int(average),
-                           _ptr(master), _ptr(m), _ptr(v), int(mv_bf16), _ptr(param_bf16),
-                           hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
-                           hp["max_norm"], int(hp["step"]), _ptr(rank_sumsq), rank_sumsq.size,
-                           int(my_rank), _ptr(scratch), _ptr(info))
+    rc = lib().oracle_step_v(ctypes.cast(keep, ctypes.c_void_p), len(grads), n, int(average),
+                             _ptr(master), _ptr(m), _ptr(v), int(mv_bf16), _ptr(param_bf16),
+                             hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+                             hp["max_norm"], int(hp["step"]), _ptr(rank_sumsq), rank_sumsq.size,
+                             int(my_rank), _ptr(scratch), _ptr(info), int(variant))
     if rc != 0:
         raise RuntimeError("oracle: the CPU flushes subnormals (FTZ/DAZ set)")
     return StepInfo(info)

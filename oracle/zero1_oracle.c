@@ -257,76 +257,108 @@ void oracle_adamw_scalars(double lr, double beta1, double beta2, double eps,
  *   p <- p - step_size * m / (sqrt(v) + eps)
  *   p <- p * (1 - lr*weight_decay)        (update first, then decay)
  * and the bf16 parameter the forward pass reads is the nearest bf16 of the
- * new fp32 master ([PT]: the fp32 master receives the update and a bf16 copy
- * is made every step).  g is the (possibly clipped) reduced gradient.
+ * new master ([PT]: the fp32 master receives the update and a bf16 copy is
+ * made every step).  g is the (possibly clipped) reduced gradient.
+ * decay_first = 1 swaps the last two lines (decay, then update): the order
+ * the page attributes to torch.optim.AdamW, which it says differs by a term
+ * of order lr^2 * lambda per step.
  */
 static void adamw_one(float g, float* p, float* m, float* v,
-                      const oracle_scalars* s)
+                      const oracle_scalars* s, int decay_first)
 {
     float mn = s->b1 * *m + s->a1 * g;
     float vn = s->b2 * *v + s->a2 * (g * g);
     float d = sqrtf(vn) + s->eps;
     float q = mn / d;
-    float pn = *p - s->sigma * q;
-    pn = pn * s->delta;
+    float pn;
+    if (decay_first) {
+        pn = *p * s->delta;
+        pn = pn - s->sigma * q;
+    } else {
+        pn = *p - s->sigma * q;
+        pn = pn * s->delta;
+    }
     *m = mn;
     *v = vn;
     *p = pn;
 }
 
 /*
- * AdamW over a flat shard with fp32 m and v.  `clip` and `coef` come from
- * oracle_clip_coef: when clip is 1 the gradient is multiplied by coef first.
+ * AdamW over a flat shard.  `clip` and `coef` come from oracle_clip_coef:
+ * when clip is 1 the gradient is multiplied by coef first.  With mv_bf16 the
+ * moments are stored as bf16 ([PT] notes that some setups keep m and v in
+ * bf16, 12 B/param in total); reading adopted: the stored bf16 moments are
+ * widened, the step runs in fp32 exactly as above, and the new moments are
+ * stored as their nearest bf16; the parameter update uses the fp32 moments.
  */
+void oracle_adamw_v(const float* g, float* master, void* m, void* v,
+                    uint16_t* param_bf16, int64_t len, const oracle_scalars* s,
+                    int clip, float coef, int mv_bf16, int decay_first)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < len; ++i) {
+        float gi = clip ? g[i] * coef : g[i];
+        if (mv_bf16) {
+            uint16_t* mb = (uint16_t*)m;
+            uint16_t* vb = (uint16_t*)v;
+            float mi = bf16_to_f32(mb[i]);
+            float vi = bf16_to_f32(vb[i]);
+            adamw_one(gi, &master[i], &mi, &vi, s, decay_first);
+            mb[i] = oracle_f32_to_bf16(mi);
+            vb[i] = oracle_f32_to_bf16(vi);
+        } else {
+            adamw_one(gi, &master[i], &((float*)m)[i], &((float*)v)[i], s, decay_first);
+        }
+        param_bf16[i] = oracle_f32_to_bf16(master[i]);
+    }
+}
+
 void oracle_adamw(const float* g, float* master, float* m, float* v,
                   uint16_t* param_bf16, int64_t len, const oracle_scalars* s,
                   int clip, float coef)
 {
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < len; ++i) {
-        float gi = clip ? g[i] * coef : g[i];
-        adamw_one(gi, &master[i], &m[i], &v[i], s);
-        param_bf16[i] = oracle_f32_to_bf16(master[i]);
-    }
+    oracle_adamw_v(g, master, m, v, param_bf16, len, s, clip, coef, 0, 0);
 }
 
-/*
- * Variant with m and v stored as bf16 ([PT] notes that some setups keep m and
- * v in bf16, 12 B/param in total).  Reading adopted: the stored bf16 moments
- * are widened, the step runs in fp32 exactly as above, and the new moments are
- * stored as their nearest bf16.  The parameter update uses the fp32 moments.
- */
 void oracle_adamw_bf16mv(const float* g, float* master, uint16_t* m_bf16,
                          uint16_t* v_bf16, uint16_t* param_bf16, int64_t len,
                          const oracle_scalars* s, int clip, float coef)
 {
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < len; ++i) {
-        float gi = clip ? g[i] * coef : g[i];
-        float mi = bf16_to_f32(m_bf16[i]);
-        float vi = bf16_to_f32(v_bf16[i]);
-        adamw_one(gi, &master[i], &mi, &vi, s);
-        m_bf16[i] = oracle_f32_to_bf16(mi);
-        v_bf16[i] = oracle_f32_to_bf16(vi);
-        param_bf16[i] = oracle_f32_to_bf16(master[i]);
-    }
+    oracle_adamw_v(g, master, m_bf16, v_bf16, param_bf16, len, s, clip, coef, 1, 0);
 }
 
-/* Torch's order (decay first, then the Adam update), used only to check the
- * page's remark that the two orders differ by a term of order lr^2*lambda. */
+/* Decay first, then the Adam update (no bf16 copy): used by the pin of the
+ * page's remark about the two orders. */
 void oracle_adamw_decay_first(const float* g, float* master, float* m, float* v,
                               int64_t len, const oracle_scalars* s)
 {
-    for (int64_t i = 0; i < len; ++i) {
-        float p = master[i] * s->delta;
-        float mn = s->b1 * m[i] + s->a1 * g[i];
-        float vn = s->b2 * v[i] + s->a2 * (g[i] * g[i]);
-        float d = sqrtf(vn) + s->eps;
-        float q = mn / d;
-        master[i] = p - s->sigma * q;
-        m[i] = mn;
-        v[i] = vn;
+    for (int64_t i = 0; i < len; ++i)
+        adamw_one(g[i], &master[i], &m[i], &v[i], s, 1);
+}
+
+/*
+ * Clip coefficient with the convention of torch.nn.utils.clip_grad_norm_
+ * (not the pages'): coef = max_norm / (norm + 1e-6), clamped at 1, i.e. the
+ * gradients are scaled only when that quotient is below 1.  Formed in fp64,
+ * rounded once to fp32.
+ */
+int oracle_clip_coef_eps(double norm, double max_norm, float* coef)
+{
+    double c = max_norm / (norm + 1e-6);
+    if (c < 1.0) {
+        *coef = (float)c;
+        return 1;
     }
+    *coef = 1.0f;
+    return 0;
+}
+
+/* The reduced gradient rounded to bf16 (nearest even) and widened back: what
+ * a reduce-scatter that delivers bf16 would hand to the optimizer. */
+void oracle_round_to_bf16(float* g, int64_t len)
+{
+    for (int64_t i = 0; i < len; ++i)
+        g[i] = bf16_to_f32(oracle_f32_to_bf16(g[i]));
 }
 
 /* ---------------------------------------------------------------------- */
@@ -341,8 +373,39 @@ void oracle_adamw_decay_first(const float* g, float* master, float* m, float* v,
  *   norm = sqrt(sum over ranks);  clip;  AdamW;  bf16 copy.
  * rank_sumsq holds the other ranks' partials on entry (zero where unknown).
  * g_scratch has len floats.  info_out receives {norm, clip coef, clip flag,
- * this rank's partial}.  Returns 0, or -1 when subnormals would be flushed.
+ * this rank's partial}.  variant: bit 0 decay first, bit 1 the torch clip
+ * convention, bit 2 the reduced gradient rounded to bf16 (compatibility
+ * variants; 0 is the pages' step).  Returns 0, or -1 when subnormals would be
+ * flushed.
  */
+int oracle_step_v(const uint16_t* const* grads, int W, int64_t len, int average,
+                  float* master, void* m, void* v, int mv_bf16,
+                  uint16_t* param_bf16, double lr, double beta1, double beta2,
+                  double eps, double weight_decay, double max_norm, int64_t t,
+                  double* rank_sumsq, int n_ranks, int my_rank, float* g_scratch,
+                  double* info_out, unsigned variant)
+{
+    if (!oracle_fp_env_ok())
+        return -1;
+    oracle_shard_reduce(grads, W, len, average, g_scratch);
+    if (variant & 4u)
+        oracle_round_to_bf16(g_scratch, len);
+    rank_sumsq[my_rank] = oracle_sumsq(g_scratch, len, 0.0);
+    double norm = oracle_global_norm(rank_sumsq, n_ranks);
+    float coef;
+    int clip = (variant & 2u) ? oracle_clip_coef_eps(norm, max_norm, &coef)
+                              : oracle_clip_coef(norm, max_norm, &coef);
+    oracle_scalars s;
+    oracle_adamw_scalars(lr, beta1, beta2, eps, weight_decay, t, &s);
+    oracle_adamw_v(g_scratch, master, m, v, param_bf16, len, &s, clip, coef,
+                   mv_bf16, (int)(variant & 1u));
+    info_out[0] = norm;
+    info_out[1] = (double)coef;
+    info_out[2] = (double)clip;
+    info_out[3] = rank_sumsq[my_rank];
+    return 0;
+}
+
 int oracle_step(const uint16_t* const* grads, int W, int64_t len, int average,
                 float* master, void* m, void* v, int mv_bf16,
                 uint16_t* param_bf16, double lr, double beta1, double beta2,
@@ -350,26 +413,9 @@ int oracle_step(const uint16_t* const* grads, int W, int64_t len, int average,
                 double* rank_sumsq, int n_ranks, int my_rank, float* g_scratch,
                 double* info_out)
 {
-    if (!oracle_fp_env_ok())
-        return -1;
-    oracle_shard_reduce(grads, W, len, average, g_scratch);
-    rank_sumsq[my_rank] = oracle_sumsq(g_scratch, len, 0.0);
-    double norm = oracle_global_norm(rank_sumsq, n_ranks);
-    float coef;
-    int clip = oracle_clip_coef(norm, max_norm, &coef);
-    oracle_scalars s;
-    oracle_adamw_scalars(lr, beta1, beta2, eps, weight_decay, t, &s);
-    if (mv_bf16)
-        oracle_adamw_bf16mv(g_scratch, master, (uint16_t*)m, (uint16_t*)v,
-                            param_bf16, len, &s, clip, coef);
-    else
-        oracle_adamw(g_scratch, master, (float*)m, (float*)v, param_bf16, len,
-                     &s, clip, coef);
-    info_out[0] = norm;
-    info_out[1] = (double)coef;
-    info_out[2] = (double)clip;
-    info_out[3] = rank_sumsq[my_rank];
-    return 0;
+    return oracle_step_v(grads, W, len, average, master, m, v, mv_bf16, param_bf16,
+                         lr, beta1, beta2, eps, weight_decay, max_norm, t,
+                         rank_sumsq, n_ranks, my_rank, g_scratch, info_out, 0u);
 }
 
 /* ---------------------------------------------------------------------- */

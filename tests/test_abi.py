@@ -170,3 +170,11 @@ def test_workload_shapes():
     ps = z.shard_pieces(numels, b, e)
     assert len(ps) == 40 and min(p[3] for p in ps) == 2048
     assert all(p[2] % 8 == 0 and p[3] % 8 == 0 for p in ps)
+
+
+def test_unknown_flags_are_rejected():
+    g = [FAKE + 4096 * k for k in range(2)]
+    assert "unknown flag" in _einval(lambda: z.shard_reduce(g, 0, 10, g_out=FAKE + (1 << 30), flags=0x1000, stream=0))
+    bufs = [FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20)]
+    assert "unknown flag" in _einval(lambda: z.adamw_step(FAKE + (4 << 20), None, 0, 100, *bufs, _hp(),
+                                                          FAKE + (5 << 20), 1, flags=0x100, stream=0))

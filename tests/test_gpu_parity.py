@@ -201,8 +201,15 @@ def ragged_for(design):
     return RAGGED8 if design == z.ONCHIP else RAGGED
 
 
+VARIANT_FLAGS = {oracle.DECAY_FIRST: z.DECAY_FIRST, oracle.CLIP_EPS: z.CLIP_EPS, oracle.G_BF16: z.G_BF16}
+
+
+def lib_flags(variant):
+    return sum(f for v, f in VARIANT_FLAGS.items() if variant & v)
+
+
 def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_state, sigma_fn,
-                      max_norm=1.0, ranks=None):
+                      max_norm=1.0, ranks=None, variant=0):
     N = sum(numels)
     ranks = list(range(W)) if ranks is None else ranks
     master_full = synth.f32(N, synth.master_key(seed), 0, 0.02)
@@ -219,9 +226,12 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
         part = np.zeros(W)
         for r in range(W):
             b, e = shard_range(N, W, r)
-            part[r] = oracle.sumsq(oracle.shard_reduce([g[b:e] for g in G]))
+            gr = oracle.shard_reduce([g[b:e] for g in G])
+            if variant & oracle.G_BF16:
+                gr = oracle.round_to_bf16(gr)
+            part[r] = oracle.sumsq(gr)
             # every rank's partial from the GPU (what the mid-step exchange would deliver)
-            z.shard_reduce(gd, b, e - b, sumsq_out=rsd[r:r + 1], ws=ws_r)
+            z.shard_reduce(gd, b, e - b, sumsq_out=rsd[r:r + 1], flags=lib_flags(variant), ws=ws_r)
         torch.cuda.synchronize()
         gpu_part = rsd.cpu().numpy().copy()
         for r in range(W):
@@ -230,9 +240,11 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
         for r in ranks:
             b, e = shard_range(N, W, r)
             rs = part.copy()
-            oi = oracle.step([g[b:e] for g in G], ost[r].master, ost[r].m, ost[r].v, ost[r].param, hp, rs, r)
+            oi = oracle.step([g[b:e] for g in G], ost[r].master, ost[r].m, ost[r].v, ost[r].param, hp, rs, r,
+                             variant=variant)
             rsd.copy_(torch.from_numpy(gpu_part))
-            z.mta_step(gd, b, shards[r].plan, hp, rsd, W, r, flags=flags, info_out=infos[r], ws=wss[r])
+            z.mta_step(gd, b, shards[r].plan, hp, rsd, W, r, flags=flags | lib_flags(variant), info_out=infos[r],
+                       ws=wss[r])
             torch.cuda.synchronize()
             ni = infos[r].cpu().numpy()
             assert rel_close(ni[1], oi.norm, NORM_TOL)
@@ -241,7 +253,7 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
             assert rel_close(rsd[r].item(), part[r], NORM_TOL)
     for r in ranks:
         master, m, v, param = shards[r].gather()
-        what = f"rank {r}/{W} flags={flags} bf16mv={mv_bf16} flat={flat_state}"
+        what = f"rank {r}/{W} flags={flags} bf16mv={mv_bf16} flat={flat_state} variant={variant}"
         assert_f32_equal(master, ost[r].master, "master " + what)
         if mv_bf16:
             assert_bf16_equal(m, ost[r].m, "m " + what)
@@ -268,6 +280,69 @@ def test_mta_parity_state_layouts(env, mv_bf16, flat_state):
     for design in (z.ONCHIP, z.STORE_G, z.RECOMPUTE_G):
         run_mta_all_ranks(torch, dev, ragged_for(design), 4, 3, 0xB000, design, mv_bf16, flat_state,
                           lambda t: [0.02, 1e-4, 0.3][t % 3])
+
+
+@pytest.mark.parametrize("variant", [oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
+                                     oracle.DECAY_FIRST | oracle.CLIP_EPS | oracle.G_BF16])
+@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+def test_compat_variants_parity(env, variant, design):
+    """Decay-first order, the torch clip convention and a bf16 reduced
+    gradient (with bf16 moments), each against the oracle's variant, every
+    rank, 3 steps, all three step designs."""
+    torch, dev = env
+    run_mta_all_ranks(torch, dev, RAGGED8, 4, 3, 0xD000 + variant, design, variant == oracle.G_BF16, True,
+                      lambda t: [0.02, 1e-4, 0.3][t % 3], variant=variant)
+
+
+def test_compat_variants_flat_adamw(env):
+    """The same variants through zero1_shard_reduce + zero1_adamw_step (g given,
+    and g recomputed from the slices).  In step 2 max_norm equals that step's
+    norm exactly: the pages' strict test does not clip, the torch convention
+    (norm + 1e-6 in the denominator) does."""
+    torch, dev = env
+    W, N = 3, 70001
+    for variant in (oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16, 7):
+        fl = lib_flags(variant)
+        master0 = synth.f32(N, synth.master_key(77), 0, 0.02)
+        for recompute in (False, True):
+            gm = torch.from_numpy(master0.copy()).to(dev)
+            gmm = torch.zeros(N, dtype=torch.float32, device=dev)
+            gvv = torch.zeros(N, dtype=torch.float32, device=dev)
+            gp = torch.zeros(N, dtype=torch.int16, device=dev)
+            om, ov, omaster, oparam = (np.zeros(N, np.float32), np.zeros(N, np.float32), master0.copy(),
+                                       np.zeros(N, np.uint16))
+            ws = ws_tensor(torch, z.workspace_bytes(N, W), dev)
+            gbuf = torch.empty(N, dtype=torch.float32, device=dev)
+            for t in range(1, 4):
+                G = replicas(77 + variant, t, W, N, [0.02, 0.3, 1e-4][t % 3])
+                gd = [to_dev_u16(torch, x, dev) for x in G]
+                g_o = oracle.shard_reduce(G)
+                if variant & oracle.G_BF16:
+                    g_o = oracle.round_to_bf16(g_o)
+                mx = oracle.global_norm([oracle.sumsq(g_o)]) if t == 2 else 1.0
+                rs = np.zeros(1)
+                oi = oracle.step(G, omaster, om, ov, oparam, hp_at(t, max_norm=mx), rs, 0, variant=variant)
+                if t == 2:
+                    assert oi.clip == bool(variant & oracle.CLIP_EPS)
+                rsd = torch.zeros(1, dtype=torch.float64, device=dev)
+                info = torch.zeros(4, dtype=torch.float64, device=dev)
+                z.shard_reduce(gd, 0, N, g_out=gbuf, sumsq_out=rsd, flags=fl, ws=ws)
+                rsd.copy_(torch.from_numpy(rs))      # the oracle's partial, so that the norm is the same
+                if recompute:
+                    z.adamw_step(None, gd, 0, N, gm, gmm, gvv, gp, hp_at(t, max_norm=mx), rsd, 1, flags=fl,
+                                 info_out=info)
+                else:
+                    z.adamw_step(gbuf, None, 0, N, gm, gmm, gvv, gp, hp_at(t, max_norm=mx), rsd, 1, flags=fl,
+                                 info_out=info)
+                torch.cuda.synchronize()
+                ni = info.cpu().numpy()
+                assert rel_close(ni[1], oi.norm, NORM_TOL)
+                assert bool(ni[2:4].view(np.int32)[1]) == oi.clip and ni[2:3].view(np.float32)[0] == oi.coef
+            what = f"flat variant={variant} recompute={recompute}"
+            assert_f32_equal(gm.cpu().numpy(), omaster, "master " + what)
+            assert_f32_equal(gmm.cpu().numpy(), om, "m " + what)
+            assert_f32_equal(gvv.cpu().numpy(), ov, "v " + what)
+            assert_bf16_equal(to_np_u16(gp), oparam, "param " + what)
 
 
 def test_mta_misaligned_pieces(env):

@@ -441,3 +441,85 @@ def test_rne_against_softfloat_samples():
         if xi < 0 or (xi == 0 and struct.pack("<f", xi)[3] & 0x80):
             ref |= 0x8000
         assert oi == ref, (xi, hex(oi), hex(ref))
+
+
+# ------------------------------------------------------------------ compatibility variants
+def test_decay_first_closed_form_and_gap():
+    """Decay-first order (the order the page attributes to torch.optim.AdamW):
+    under a constant gradient p_t = p_{t-1}*(1-lr*wd) - u_t, and over many
+    steps the two orders drift apart by the sum of sigma_t*|q_t|*lr*wd (the
+    page's 'order lr^2*lambda per step'), here on the quadratic f(x) = x^2/2."""
+    lr, wd = 1e-3, 0.1
+    gval = 2.0 ** -7
+    g = _bf16_of([gval])
+    p = np.array([0.25], np.float32)
+    m = np.zeros(1, np.float32)
+    v = np.zeros(1, np.float32)
+    p64 = 0.25
+    for t in range(1, 11):
+        oracle.step([g], p, m, v, oracle.f32_to_bf16(p), hp_at(t, max_norm=math.inf), np.zeros(1), 0,
+                    variant=oracle.DECAY_FIRST)
+        bc2 = 1 - 0.95 ** t
+        u = lr * gval * math.sqrt(bc2) / (math.sqrt(bc2) * gval + 1e-8)
+        p64 = p64 * (1 - lr * wd) - u
+        assert abs(float(p[0]) - p64) <= 1e-6 * abs(p64)
+    # quadratic: gradient = x (fed as an exact bf16 value each step), both orders
+    xs = {}
+    for var in (0, oracle.DECAY_FIRST):
+        x = np.array([1.0], np.float32)
+        m = np.zeros(1, np.float32)
+        v = np.zeros(1, np.float32)
+        bound = 0.0
+        for t in range(1, 101):
+            gb = oracle.f32_to_bf16(x.copy())
+            s = oracle.adamw_scalars(lr, 0.9, 0.95, 1e-8, wd, t)
+            # |m/(sqrt(v)+eps)| stays below ~3 for Adam with these betas
+            bound += float(s.sigma) * 3.0 * lr * wd * (1 + abs(float(x[0])))
+            oracle.step([gb], x, m, v, oracle.f32_to_bf16(x), hp_at(t, max_norm=math.inf), np.zeros(1), 0,
+                        variant=var)
+        xs[var] = float(x[0])
+    gap = abs(xs[0] - xs[oracle.DECAY_FIRST])
+    assert 0 < gap <= bound + 1e-6
+
+
+def test_torch_clip_convention_against_torch():
+    """The torch clip variant reproduces torch.nn.utils.clip_grad_norm_'s
+    coefficient (max_norm / (norm + 1e-6), clamped at 1; fp64 gradients)."""
+    torch = pytest.importorskip("torch")
+    for norm_target, max_norm in [(1.25, 1.0), (0.5, 1.0), (1.0, 1.0), (3.0e5, 2.0)]:
+        x = torch.zeros(3, dtype=torch.float64)
+        x[0] = 1.0
+        x[1] = math.sqrt(norm_target ** 2 - 1.0) if norm_target > 1 else 0.0
+        if norm_target <= 1:
+            x[0] = norm_target
+        nrm = float(torch.linalg.vector_norm(x))
+        p = torch.nn.Parameter(torch.zeros(3, dtype=torch.float64))
+        p.grad = x.clone()
+        torch.nn.utils.clip_grad_norm_([p], max_norm)
+        torch_coef = float(p.grad[0] / x[0])
+        clip, coef = oracle.clip_coef_eps(nrm, max_norm)
+        assert coef == np.float32(torch_coef), (norm_target, coef, torch_coef)
+        assert clip == (torch_coef < 1.0)
+    # at the threshold the torch convention clips (slightly), the pages' does not
+    assert oracle.clip_coef_eps(1.0, 1.0)[0] and not oracle.clip_coef(1.0, 1.0)[0]
+
+
+def test_g_bf16_variant_is_a_step_on_the_rounded_gradient():
+    """Rounding the reduced gradient to bf16 before the norm and the update is
+    the same as one plain step whose single replica is that bf16 gradient."""
+    W, N = 5, 20000
+    G = synth_grads(0xB16, 1, W, N, 0.3, outlier_pct=2)
+    gb = oracle.f32_to_bf16(oracle.shard_reduce(G))
+    assert np.array_equal(oracle.bf16_to_f32(gb), oracle.round_to_bf16(oracle.shard_reduce(G)))
+    master = synth.f32(N, synth.master_key(3), 0, 0.02)
+    a = [master.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32), np.zeros(N, np.uint16)]
+    b = [master.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32), np.zeros(N, np.uint16)]
+    ia = oracle.step(G, *a, hp_at(1), np.zeros(1), 0, variant=oracle.G_BF16)
+    ib = oracle.step([gb], *b, hp_at(1), np.zeros(1), 0)
+    assert ia.norm == ib.norm and ia.coef == ib.coef and ia.clip
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    # and it differs from the fp32-gradient step
+    c = [master.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32), np.zeros(N, np.uint16)]
+    oracle.step(G, *c, hp_at(1), np.zeros(1), 0)
+    assert not np.array_equal(c[0], a[0])

@@ -19,6 +19,9 @@ MV_BF16 = 0x2
 RECOMPUTE_G = 0x4
 STORE_G = 0x8
 ONCHIP = 0x10
+DECAY_FIRST = 0x20
+CLIP_EPS = 0x40
+G_BF16 = 0x80
 MAX_W = 128
 
 P = ctypes.c_void_p

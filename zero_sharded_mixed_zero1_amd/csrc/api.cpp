@@ -184,7 +184,7 @@ Shape reduce_shape(int64_t tiles, const DevInfo& d)
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 zero1_status check_grads(const uint16_t* const* grads, int W, int64_t begin, int64_t len, Reduce& r,
-                         bool sum_only, bool& vec_ok)
+                         uint32_t flags, bool& vec_ok)
 {
     if (W < 1 || W > kMaxW) return fail(ZERO1_EINVAL, "W=%d must be in [1, %d]", W, kMaxW);
     if (len < 0) return fail(ZERO1_EINVAL, "len=%lld is negative", (long long)len);
@@ -198,7 +198,8 @@ zero1_status check_grads(const uint16_t* const* grads, int W, int64_t begin, int
         if (!aligned16(r.gp.p[w])) vec_ok = false;
     }
     r.W = W;
-    if (sum_only || W == 1) {
+    r.round_bf16 = (flags & ZERO1_G_BF16) ? 1 : 0;
+    if ((flags & ZERO1_SUM_ONLY) || W == 1) {
         r.mode = kAvgNone;
     } else if ((W & (W - 1)) == 0) {
         r.mode = kAvgMulPow2;   // s * 2^-k == s / W exactly for a power of two
@@ -207,6 +208,16 @@ zero1_status check_grads(const uint16_t* const* grads, int W, int64_t begin, int
         r.mode = kAvgDiv;
         r.f_w = (float)W;
     }
+    return ZERO1_OK;
+}
+
+constexpr uint32_t kAllFlags = ZERO1_SUM_ONLY | ZERO1_MV_BF16 | ZERO1_RECOMPUTE_G | ZERO1_STORE_G | ZERO1_ONCHIP |
+                               ZERO1_DECAY_FIRST | ZERO1_CLIP_EPS | ZERO1_G_BF16;
+
+zero1_status check_flags(uint32_t flags, uint32_t allowed, const char* fn)
+{
+    if (flags & ~kAllFlags) return fail(ZERO1_EINVAL, "%s: unknown flag bits 0x%x", fn, flags & ~kAllFlags);
+    if (flags & ~allowed) return fail(ZERO1_EINVAL, "%s: flags 0x%x do not apply here", fn, flags & ~allowed);
     return ZERO1_OK;
 }
 
@@ -227,9 +238,10 @@ zero1_status check_hparams(const zero1_hparams* hp)
 // The page's AdamW applies Python floats to fp32 tensors: each scalar is formed
 // in double and used as the nearest binary32 ("并行训练", section on mixed
 // precision and AdamW: step_size = lr*sqrt(1-beta2^t)/(1-beta1^t), decay 1-lr*wd).
-Scal scalars(const zero1_hparams* hp)
+Scal scalars(const zero1_hparams* hp, uint32_t flags)
 {
     Scal s;
+    s.decay_first = (flags & ZERO1_DECAY_FIRST) ? 1 : 0;
     s.b1 = (float)hp->beta1;
     s.b2 = (float)hp->beta2;
     s.a1 = (float)(1.0 - hp->beta1);
@@ -306,9 +318,10 @@ zero1_status zero1_shard_reduce(const uint16_t* const* grads, int W, int64_t beg
                                 uint32_t flags, float* g_out, double* sumsq_out, void* ws,
                                 size_t ws_bytes, void* stream)
 {
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_shard_reduce")) return fs;
     Reduce r;
     bool vec = false;
-    zero1_status st = check_grads(grads, W, begin, len, r, (flags & ZERO1_SUM_ONLY) != 0, vec);
+    zero1_status st = check_grads(grads, W, begin, len, r, flags, vec);
     if (st) return st;
     if (!g_out && !sumsq_out) return fail(ZERO1_EINVAL, "g_out and sumsq_out are both NULL");
     if (g_out) {
@@ -364,6 +377,7 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
                               const double* rank_sumsq, int n_ranks, uint32_t flags, zero1_norm_info* info_out,
                               void* stream)
 {
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_adamw_step")) return fs;
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
     if (len < 0) return fail(ZERO1_EINVAL, "len=%lld is negative", (long long)len);
@@ -374,7 +388,7 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
     std::memset(&r, 0, sizeof r);
     bool vec = true;
     if (!g) {
-        if ((st = check_grads(grads, W, begin, len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
+        if ((st = check_grads(grads, W, begin, len, r, flags, vec))) return st;
     } else if (!aligned16(g)) {
         vec = false;
     }
@@ -395,11 +409,12 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
     if ((st = current_device(d))) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // always launched (also for len == 0) so that info_out is written
-    const Scal sc = scalars(hp);
+    const Scal sc = scalars(hp, flags);
     const Shape sh = update_shape(tiles(len, vec), d);
     const int nb = sh.grid;
     Z1_HIP(launch_adamw_flat(g, r, len, vec, mv_bf16, master, m, v, param_bf16, sc, rank_sumsq, n_ranks,
-                             hp->max_norm, reinterpret_cast<NormInfo*>(info_out), nb, sh.split, s));
+                             hp->max_norm, (flags & ZERO1_CLIP_EPS) ? 1 : 0,
+                             reinterpret_cast<NormInfo*>(info_out), nb, sh.split, s));
     return finish(s);
 }
 
@@ -429,6 +444,7 @@ size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces)
 zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t flags, void* table,
                             size_t table_bytes, zero1_plan* plan_out)
 {
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_plan")) return fs;
     if (!plan_out) return fail(ZERO1_EINVAL, "plan_out is NULL");
     if (!pieces || n_pieces < 1) return fail(ZERO1_EINVAL, "need at least one piece");
     const bool mv_bf16 = (flags & ZERO1_MV_BF16) != 0;
@@ -546,7 +562,7 @@ static zero1_status mta_common(const uint16_t* const* grads, int W, int64_t begi
     const uint32_t designs = flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
     if (designs & (designs - 1))
         return fail(ZERO1_EINVAL, "ZERO1_STORE_G, ZERO1_RECOMPUTE_G and ZERO1_ONCHIP are exclusive");
-    if ((st = check_grads(grads, W, begin, plan->shard_len, r, (flags & ZERO1_SUM_ONLY) != 0, vec))) return st;
+    if ((st = check_grads(grads, W, begin, plan->shard_len, r, flags, vec))) return st;
     vec = vec && plan->aligned;
     store_g = use_store_g(flags, W);
     if ((st = current_device(d))) return st;
@@ -556,6 +572,7 @@ static zero1_status mta_common(const uint16_t* const* grads, int W, int64_t begi
 zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
                               double* sumsq_out, uint32_t flags, void* ws, size_t ws_bytes, void* stream)
 {
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_reduce")) return fs;
     Reduce r;
     bool vec = false, store_g = false;
     DevInfo d;
@@ -576,6 +593,7 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
                               const zero1_hparams* hp, const double* rank_sumsq, int n_ranks, uint32_t flags,
                               zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
 {
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_update")) return fs;
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
     if (n_ranks < 1) return fail(ZERO1_EINVAL, "n_ranks=%d must be >= 1", n_ranks);
@@ -592,8 +610,9 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
     const ChunkDesc* cd = reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
     const Shape sh = update_shape(plan->n_chunks, d);
     const int nb = sh.grid;
-    Z1_HIP(launch_adamw_mta(w.g, r, pd, cd, plan->n_chunks, vec, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp),
-                            rank_sumsq, n_ranks, hp->max_norm, reinterpret_cast<NormInfo*>(info_out), nb, sh.split, s));
+    Z1_HIP(launch_adamw_mta(w.g, r, pd, cd, plan->n_chunks, vec, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp, flags),
+                            rank_sumsq, n_ranks, hp->max_norm, (flags & ZERO1_CLIP_EPS) ? 1 : 0,
+                            reinterpret_cast<NormInfo*>(info_out), nb, sh.split, s));
     return finish(s);
 }
 
@@ -604,7 +623,7 @@ int zero1_mta_design(const uint16_t* const* grads, int W, int64_t begin, const z
     if (designs & (designs - 1)) return 0;
     Reduce r;
     bool vec = false;
-    if (check_grads(grads, W, begin, plan->shard_len, r, false, vec) != ZERO1_OK) return 0;
+    if (check_grads(grads, W, begin, plan->shard_len, r, 0, vec) != ZERO1_OK) return 0;
     vec = vec && plan->aligned;
     if (flags & ZERO1_STORE_G) return ZERO1_STORE_G;
     if (flags & ZERO1_RECOMPUTE_G) return ZERO1_RECOMPUTE_G;
@@ -621,6 +640,7 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
                             const zero1_hparams* hp, double* rank_sumsq, int n_ranks, int my_rank,
                             uint32_t flags, zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
 {
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_step")) return fs;
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
     if (n_ranks < 1 || my_rank < 0 || my_rank >= n_ranks)
@@ -640,9 +660,9 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
             const PieceDesc* pd = reinterpret_cast<const PieceDesc*>(tb);
             const ChunkDesc* cd =
                 reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
-            Z1_HIP(launch_onchip(k, r, pd, cd, plan->n_chunks, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp),
+            Z1_HIP(launch_onchip(k, r, pd, cd, plan->n_chunks, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp, flags),
                                  w.partials, rank_sumsq, n_ranks, my_rank, hp->max_norm,
-                                 reinterpret_cast<NormInfo*>(info_out), grid, s));
+                                 (flags & ZERO1_CLIP_EPS) ? 1 : 0, reinterpret_cast<NormInfo*>(info_out), grid, s));
             return finish(s);
         }
         return fail(ZERO1_EINVAL, "ZERO1_ONCHIP: the shard (%lld elements, %d chunks) does not fit in one "

@@ -23,6 +23,7 @@ struct GradPtrs {
 // Per-step fp32 scalars, formed in fp64 on the host and rounded once.
 struct Scal {
     float b1, b2, a1, a2, eps, sigma, delta;
+    int decay_first;   // 1: decay the master before the Adam update
 };
 
 // How the W-slice sum becomes g: keep it, multiply by the exact 2^-k (W a
@@ -35,6 +36,7 @@ struct Reduce {
     int mode;      // AvgMode
     float inv_w;   // 2^-k for kAvgMulPow2
     float f_w;     // (float)W for kAvgDiv
+    int round_bf16;  // 1: g is rounded to the nearest bf16 after the average
 };
 
 // Same layout as zero1_norm_info.
@@ -78,16 +80,17 @@ hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, h
 // Phase 2 over a flat shard.  g == nullptr: recompute g from r.  Every
 // workgroup first forms the global norm from rank_sumsq[0..n_ranks) (in rank
 // order) and the clip decision for max_norm; workgroup 0 writes it to info_out.
+// clip_eps selects the torch clip convention (max_norm / (norm + 1e-6) < 1).
 hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool vec,
                              bool mv_bf16, float* master, void* m, void* v,
                              uint16_t* param, const Scal& sc, const double* rank_sumsq,
-                             int n_ranks, double max_norm, NormInfo* info_out,
+                             int n_ranks, double max_norm, int clip_eps, NormInfo* info_out,
                              int nblocks, int split, hipStream_t s);
 // Phase 2 over a multi-tensor plan (same prologue).
 hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces,
                             const ChunkDesc* chunks, int n_chunks, bool vec,
                             bool mv_bf16, const Scal& sc, const double* rank_sumsq,
-                            int n_ranks, double max_norm, NormInfo* info_out,
+                            int n_ranks, double max_norm, int clip_eps, NormInfo* info_out,
                             int nblocks, int split, hipStream_t s);
 // Single-launch step (cooperative grid barrier) for shards whose reduced
 // gradient fits in registers: K tiles per workgroup.
@@ -95,6 +98,7 @@ int onchip_variants(int* ks, int max_n);
 hipError_t onchip_max_blocks(int k, bool mv_bf16, int* blocks_per_cu);
 hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks, int n_chunks,
                          bool mv_bf16, const Scal& sc, double* partials, double* rank_sumsq, int n_ranks,
-                         int my_rank, double max_norm, NormInfo* info_out, int nblocks, hipStream_t s);
+                         int my_rank, double max_norm, int clip_eps, NormInfo* info_out, int nblocks,
+                         hipStream_t s);
 
 }  // namespace z1

@@ -173,8 +173,11 @@ __device__ __forceinline__ void st8_f32(float* p, const float (&x)[8])
 // then the average (multiply by the exact 2^-k, or an IEEE division).
 __device__ __forceinline__ float average(const Reduce& r, float s)
 {
-    if (r.mode == kAvgMulPow2) return s * r.inv_w;
-    if (r.mode == kAvgDiv) return s / r.f_w;
+    if (r.mode == kAvgMulPow2) s = s * r.inv_w;
+    else if (r.mode == kAvgDiv) s = s / r.f_w;
+    // compatibility variant: the reduced gradient as a bf16 reduce-scatter
+    // would deliver it (nearest even), widened back for the update
+    if (r.round_bf16) s = __uint_as_float(bf16_rne_bits(s) << 16);
     return s;
 }
 
@@ -315,27 +318,32 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const double* __rest
     if (threadIdx.x == 0) *q_out = sh[0];
 }
 
-// Global norm and clip decision from the ranks' partial sums of squares
-// ("训练循环与 checkpoint": clip all gradients as one vector when the L2 norm
-// exceeds max_norm).  The partials are added in rank order, so every
-// workgroup that evaluates this gets the same bits.
-__device__ __forceinline__ NormInfo clip_info(const double* rank_sumsq, int n_ranks, double max_norm)
+// Global norm and clip decision from the sum of the ranks' partial sums of
+// squares ("训练循环与 checkpoint": clip all gradients as one vector when the
+// L2 norm exceeds max_norm).  clip_eps selects the torch convention instead:
+// coefficient max_norm / (norm + 1e-6), applied when it is below 1.
+__device__ __forceinline__ NormInfo norm_info(double tot, double max_norm, int clip_eps)
 {
     NormInfo ni;
-    double tot = 0.0;
-    for (int q = 0; q < n_ranks; ++q) tot = tot + rank_sumsq[q];
     ni.sumsq_total = tot;
     ni.norm = sqrt(tot);
-    if (ni.norm > max_norm) {
-        ni.clip = 1;
-        ni.clip_coef = (float)(max_norm / ni.norm);
-    } else {
-        ni.clip = 0;
-        ni.clip_coef = 1.0f;
-    }
+    const double c = clip_eps ? max_norm / (ni.norm + 1e-6) : max_norm / ni.norm;
+    const bool clip = clip_eps ? (c < 1.0) : (ni.norm > max_norm);
+    ni.clip = clip ? 1 : 0;
+    ni.clip_coef = clip ? (float)c : 1.0f;
     ni.nonfinite = (isnan(ni.norm) || isinf(ni.norm)) ? 1 : 0;
     ni.reserved = 0;
     return ni;
+}
+
+// The partials are added in rank order, so every workgroup that evaluates
+// this gets the same bits.
+__device__ __forceinline__ NormInfo clip_info(const double* rank_sumsq, int n_ranks, double max_norm,
+                                              int clip_eps)
+{
+    double tot = 0.0;
+    for (int q = 0; q < n_ranks; ++q) tot = tot + rank_sumsq[q];
+    return norm_info(tot, max_norm, clip_eps);
 }
 
 // Prologue of every update kernel: lane 0 forms the clip decision, workgroup 0
@@ -344,6 +352,7 @@ struct ClipArgs {
     const double* rank_sumsq;
     int n_ranks;
     double max_norm;
+    int clip_eps;
     NormInfo* info_out;   // may be null
 };
 
@@ -351,7 +360,7 @@ __device__ __forceinline__ void block_clip(const ClipArgs& ca, bool& clip, float
 {
     __shared__ NormInfo sh;
     if (threadIdx.x == 0) {
-        sh = clip_info(ca.rank_sumsq, ca.n_ranks, ca.max_norm);
+        sh = clip_info(ca.rank_sumsq, ca.n_ranks, ca.max_norm, ca.clip_eps);
         if (blockIdx.x == 0 && ca.info_out) *ca.info_out = sh;
     }
     __syncthreads();
@@ -367,8 +376,14 @@ __device__ __forceinline__ void adamw_elem(float g, float& p, float& m, float& v
     const float vn = c.b2 * v + c.a2 * (g * g);
     const float d = sqrtf(vn) + c.eps;
     const float q = mn / d;
-    float pn = p - c.sigma * q;
-    pn = pn * c.delta;
+    float pn;
+    if (c.decay_first) {   // compatibility variant: decay, then update
+        pn = p * c.delta;
+        pn = pn - c.sigma * q;
+    } else {
+        pn = p - c.sigma * q;
+        pn = pn * c.delta;
+    }
     m = mn;
     v = vn;
     p = pn;
@@ -514,6 +529,7 @@ struct OnchipArgs {
     int n_ranks;
     int my_rank;
     double max_norm;
+    int clip_eps;
     NormInfo* info_out;     // may be null
 };
 
@@ -579,20 +595,9 @@ __global__ __launch_bounds__(kThreads, MINW) void onchip_step_kernel(Reduce r, c
     }
     if (threadIdx.x == 0) {
         const double q_r = sh[0];
-        NormInfo ni;
         double tot = 0.0;
         for (int q = 0; q < oa.n_ranks; ++q) tot = tot + (q == oa.my_rank ? q_r : oa.rank_sumsq[q]);
-        ni.sumsq_total = tot;
-        ni.norm = sqrt(tot);
-        if (ni.norm > oa.max_norm) {
-            ni.clip = 1;
-            ni.clip_coef = (float)(oa.max_norm / ni.norm);
-        } else {
-            ni.clip = 0;
-            ni.clip_coef = 1.0f;
-        }
-        ni.nonfinite = (isnan(ni.norm) || isinf(ni.norm)) ? 1 : 0;
-        ni.reserved = 0;
+        const NormInfo ni = norm_info(tot, oa.max_norm, oa.clip_eps);
         shi = ni;
         if (blockIdx.x == 0) {
             oa.rank_sumsq[oa.my_rank] = q_r;     // no workgroup reads this entry
@@ -662,11 +667,11 @@ hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, h
 
 hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool vec, bool mv_bf16,
                              float* master, void* m, void* v, uint16_t* param, const Scal& sc,
-                             const double* rank_sumsq, int n_ranks, double max_norm, NormInfo* info_out,
-                             int nblocks, int split, hipStream_t s)
+                             const double* rank_sumsq, int n_ranks, double max_norm, int clip_eps,
+                             NormInfo* info_out, int nblocks, int split, hipStream_t s)
 {
     const dim3 grid(nblocks), block(kThreads);
-    const ClipArgs ca{rank_sumsq, n_ranks, max_norm, info_out};
+    const ClipArgs ca{rank_sumsq, n_ranks, max_norm, clip_eps, info_out};
     const Span sp{g, master, m, v, param};
 #define Z1_FLAT(V, GS, MV) hipLaunchKernelGGL((adamw_flat_kernel<V, GS, MV>), grid, block, 0, s, sp, r, len, sc, ca, split)
     const int gs = g ? 0 : 1;
@@ -683,11 +688,11 @@ hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool 
 
 hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks,
                             int n_chunks, bool vec, bool mv_bf16, const Scal& sc, const double* rank_sumsq,
-                            int n_ranks, double max_norm, NormInfo* info_out, int nblocks, int split,
-                            hipStream_t s)
+                            int n_ranks, double max_norm, int clip_eps, NormInfo* info_out, int nblocks,
+                            int split, hipStream_t s)
 {
     const dim3 grid(nblocks), block(kThreads);
-    const ClipArgs ca{rank_sumsq, n_ranks, max_norm, info_out};
+    const ClipArgs ca{rank_sumsq, n_ranks, max_norm, clip_eps, info_out};
 #define Z1_MTA(V, GS, MV) hipLaunchKernelGGL((adamw_mta_kernel<V, GS, MV>), grid, block, 0, s, g, r, pieces, chunks, n_chunks, sc, ca, split)
     const int gs = g ? 0 : 1;
     if (vec) {
@@ -731,7 +736,7 @@ hipError_t onchip_max_blocks(int k, bool mv_bf16, int* blocks_per_cu)
 
 hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks, int n_chunks,
                          bool mv_bf16, const Scal& sc, double* partials, double* rank_sumsq, int n_ranks, int my_rank,
-                         double max_norm, NormInfo* info_out, int nblocks, hipStream_t s)
+                         double max_norm, int clip_eps, NormInfo* info_out, int nblocks, hipStream_t s)
 {
     const void* f = onchip_fn(k, mv_bf16);
     if (!f) return hipErrorInvalidValue;
@@ -740,7 +745,7 @@ hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const 
     const ChunkDesc* cd = chunks;
     int nc = n_chunks;
     Scal cc = sc;
-    OnchipArgs oa{partials, rank_sumsq, n_ranks, my_rank, max_norm, info_out};
+    OnchipArgs oa{partials, rank_sumsq, n_ranks, my_rank, max_norm, clip_eps, info_out};
     void* args[] = {&rr, &pd, &cd, &nc, &cc, &oa};
     return hipLaunchCooperativeKernel(f, dim3(nblocks), dim3(kThreads), args, 0, s);
 }
