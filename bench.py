@@ -20,6 +20,7 @@ Modes:
   python bench.py [--steps K] [--warmup W] [--config C2]    the benchmark line
   python bench.py --pmc-run                                   short run for rocprofv3 --pmc
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR OUT     counter summary for profiles/
+  python bench.py --summarize-kt KT_DIR OUT                   kernel-trace summary for profiles/
 """
 from __future__ import annotations
 
@@ -231,6 +232,30 @@ def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL):
     print("\n".join(lines))
 
 
+def summarize_kt(kt_dir, out_path):
+    """Per-kernel dispatch statistics from a rocprofv3 --kernel-trace output dir,
+    split by grid size (the whole-shard reduce and the bucket reduces are the
+    same kernel at different grids), appended to out_path."""
+    import statistics as stt
+    rows = {}
+    for f in glob.glob(os.path.join(kt_dir, "**", "*kernel_trace*.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                short = name.replace("void ", "").replace("z1::(anonymous namespace)::", "").split("(")[0]
+                grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                rows.setdefault((short, grid), []).append(dur)
+    lines = [f"{'kernel':<48} | {'workgroups':>10} | {'calls':>5} | {'avg_us':>8} | {'median_us':>9} | "
+             f"{'min_us':>8} | {'max_us':>8}"]
+    for (short, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{short[:48]:<48} | {grid:>10} | {len(d):>5} | {sum(d) / len(d):>8.2f} | "
+                     f"{stt.median(d):>9.2f} | {min(d):>8.2f} | {max(d):>8.2f}")
+    with open(out_path, "a") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_from_summary(path, kernel):
     """Counter bytes per launch of `kernel` from the committed summary, or None
     if the kernels changed since the counters were taken."""
@@ -250,6 +275,45 @@ def traffic_from_summary(path, kernel):
 
 
 # ---------------------------------------------------------------------- main
+def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
+    """The ZeRO-2-style flow on the same shard: the reduce runs per bucket (a
+    25 MB bucket of the whole model's bf16 gradient is 25e6 / (2 W) of this
+    rank's shard elements, rounded to whole 2048-element tiles), buckets in
+    reverse order as backward would produce them; what is left after backward
+    is the partials sum and the update.  Returns per step: the GPU time of all
+    bucket reduces (HIP events around each call, summed) and the time from the
+    last bucket to the end of the update (ms)."""
+    W, rank, S = st["W"], st["rank"], st["S"]
+    b = max(2048, bucket_bytes // (2 * W) // 2048 * 2048)
+    ranges = [(lo, min(S, lo + b)) for lo in range(0, S, b)][::-1]
+    nb = len(ranges)
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = []
+    for c in st["copies"]:
+        if not hasattr(c, "parts"):
+            c.parts = torch.zeros(nb, dtype=torch.float64, device=c.master.device)
+        # addresses prepared once, so the timed loop is one C call per bucket
+        calls.append([([g.data_ptr() + 2 * (c.begin + lo) for g in c.grads], lo, hi,
+                       c.parts.data_ptr() + 8 * (nb - 1 - i)) for i, (lo, hi) in enumerate(ranges)])
+    red_ms, crit_ms = [], []
+    for k in range(k0, k0 + steps):
+        ci = k % len(st["copies"])
+        c = st["copies"][ci]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nb + 1)]
+        for i, (gp, lo, hi, part) in enumerate(calls[ci]):
+            ev[2 * i].record()
+            z.mta_reduce_range(gp, c.plan, lo, hi, part, flags=z.STORE_G, ws=c.ws, stream=stream)
+            ev[2 * i + 1].record()
+        z.partials_sum(c.parts, nb, c.rsd[rank:rank + 1], stream=stream)
+        z.mta_update(c.grads, c.begin, c.plan, hp(cfg, k + 1), c.rsd, W, flags=z.STORE_G, ws=c.ws, stream=stream)
+        ev[2 * nb].record()
+        torch.cuda.synchronize()
+        red_ms.append(sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(nb)))
+        crit_ms.append(ev[2 * nb - 1].elapsed_time(ev[2 * nb]))
+    return dict(bucket_params=b, buckets=nb, reduce_ms=sum(red_ms) / steps,
+                after_backward_ms=sum(crit_ms) / steps)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,10 +325,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--summarize-kt", nargs=2, metavar=("KT_DIR", "OUT"))
     a = ap.parse_args()
 
     if a.summarize_pmc:
         summarize_pmc(*a.summarize_pmc)
+        return 0
+    if a.summarize_kt:
+        summarize_kt(*a.summarize_kt)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -362,6 +430,8 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": kern_bytes},
     }
+    if flags & z.STORE_G:
+        out["bucketed"] = bucketed_timing(torch, z, cfg, st, a.warmup + 2 * a.steps, min(a.steps, 50))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, S, st["begin"])
     print(json.dumps(out), flush=True)

@@ -271,6 +271,34 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
                               const double* rank_sumsq, int n_ranks, uint32_t flags,
                               zero1_norm_info* info_out, void* ws, size_t ws_bytes,
                               void* stream);
+/* ---------------------------------------------------------------- buckets
+ * Incremental reduction while backward still runs (reduce each bucket of
+ * gradients as soon as it is produced, as ZeRO stage 2 does: "并行训练",
+ * "数据并行与 ZeRO：按 batch 切，再把状态切碎"; "Stanford CS336 第七讲精读" 5.3), so
+ * that only the update is left on the optimizer step's critical path:
+ *   for each bucket k (any order):  zero1_mta_reduce_range(..., lo_k, hi_k,
+ *                                     parts + k, ZERO1_STORE_G, ws, ...)
+ *   zero1_partials_sum(parts, n_buckets, rank_sumsq + my_rank)
+ *   (multi-GPU: exchange rank_sumsq)
+ *   zero1_mta_update(..., ZERO1_STORE_G, ws, ...)
+ * The buckets must cover the shard exactly once before the update. Every call
+ * on one workspace reuses its partials area: issue them in order on one stream
+ * (calls on different streams with the same workspace race).
+ *
+ * zero1_mta_reduce_range: steps 1-2 for shard elements [lo, hi): grads[w][k]
+ *   is replica w's gradient of shard element lo + k (bf16, device); g for the
+ *   range is stored in the workspace (sized by zero1_mta_workspace_bytes(plan,
+ *   W, ZERO1_STORE_G)) and the range's fp64 sum of squares goes to *sumsq_out.
+ *   flags: ZERO1_SUM_ONLY, ZERO1_G_BF16 (RECOMPUTE_G / ONCHIP: EINVAL).
+ * zero1_partials_sum: *sum_out = parts[0] + parts[1] + ... (n <= 8192 doubles,
+ *   device), added in a fixed order (deterministic). */
+zero1_status zero1_mta_reduce_range(const uint16_t* const* grads, int W,
+                                    const zero1_plan* plan, int64_t lo, int64_t hi,
+                                    double* sumsq_out, uint32_t flags, void* ws,
+                                    size_t ws_bytes, void* stream);
+zero1_status zero1_partials_sum(const double* parts, int n, double* sum_out,
+                                void* stream);
+
 /* Which design zero1_mta_step would run for these arguments on the current
  * device: ZERO1_ONCHIP, ZERO1_STORE_G or ZERO1_RECOMPUTE_G; 0 when the
  * arguments are invalid or an explicitly requested design is impossible. */

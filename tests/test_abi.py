@@ -178,3 +178,21 @@ def test_unknown_flags_are_rejected():
     bufs = [FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20)]
     assert "unknown flag" in _einval(lambda: z.adamw_step(FAKE + (4 << 20), None, 0, 100, *bufs, _hp(),
                                                           FAKE + (5 << 20), 1, flags=0x100, stream=0))
+
+
+def test_bucketed_reduction_rejects_bad_arguments():
+    plan = z.Plan(table=FAKE, shard_len=1000, n_pieces=1, n_chunks=1, chunk_elems=2048)
+    g = [FAKE + (1 << 20) * k for k in range(4)]
+    assert "inside the shard" in _einval(lambda: z.mta_reduce_range(g, plan, 5, 3, FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "inside the shard" in _einval(lambda: z.mta_reduce_range(g, plan, -1, 3, FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "inside the shard" in _einval(lambda: z.mta_reduce_range(g, plan, 0, 1001, FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "STORE_G only" in _einval(lambda: z.mta_reduce_range(g, plan, 0, 10, FAKE, flags=z.RECOMPUTE_G,
+                                                                ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "sumsq_out" in _einval(lambda: z.mta_reduce_range(g, plan, 0, 10, 0, ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "plan" in _einval(lambda: z.mta_reduce_range(g, z.Plan(), 0, 10, FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "W=0" in _einval(lambda: z.mta_reduce_range([], plan, 0, 10, FAKE, ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "unknown" in _einval(lambda: z.mta_reduce_range(g, plan, 0, 10, FAKE, flags=1 << 20,
+                                                           ws=FAKE, ws_bytes=1 << 30, stream=0))
+    assert "n=" in _einval(lambda: z.partials_sum(FAKE, -1, FAKE, stream=0))
+    assert "n=" in _einval(lambda: z.partials_sum(FAKE, 8193, FAKE, stream=0))
+    assert "NULL" in _einval(lambda: z.partials_sum(FAKE, 4, 0, stream=0))

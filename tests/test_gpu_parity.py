@@ -531,3 +531,56 @@ def test_bf16_stagnation_on_gpu(env):
     p = to_np_u16(gp)
     assert_bf16_equal(p, oparam, "param after 1000 steps")
     assert np.all(oracle.bf16_to_f32(p) < 2e-3)
+
+
+def test_bucketed_reduction_matches_oracle_and_mta_step(env):
+    """ZeRO-2-style flow: each tensor's piece of the shard is a bucket whose W
+    gradient slices exist only while it is reduced (reduced in reverse order,
+    as backward produces them); the bucket partials are then added in order and
+    the update runs alone.  State must equal the oracle's step bit for bit."""
+    torch, dev = env
+    W, steps = 4, 3
+    numels = RAGGED8
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xE000), 0, 0.02)
+    for r in (0, 3):
+        sh = MtaShard(torch, dev, numels, W, r, master_full)
+        ws = sh.workspace(z.STORE_G)
+        from tests.oracle_sim import RankState
+        o = RankState(master_full[sh.begin:sh.begin + sh.S])
+        parts = torch.zeros(len(sh.pl), dtype=torch.float64, device=dev)
+        rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+        info = torch.zeros(4, dtype=torch.float64, device=dev)
+        for t in range(1, steps + 1):
+            G = replicas(0xE000, t, W, N, [0.02, 1e-4, 0.3][t % 3])
+            part = np.zeros(W)
+            for q in range(W):
+                b, e = shard_range(N, W, q)
+                part[q] = oracle.sumsq(oracle.shard_reduce([g[b:e] for g in G]))
+            for k in reversed(range(len(sh.pl))):
+                _, _, so, n = sh.pl[k]
+                lo = sh.begin + so
+                bucket = [to_dev_u16(torch, g[lo:lo + n].copy(), dev) for g in G]   # this bucket only
+                z.mta_reduce_range(bucket, sh.plan, so, so + n, parts[k:k + 1], flags=z.STORE_G, ws=ws)
+                del bucket
+            rsd.copy_(torch.from_numpy(part))
+            z.partials_sum(parts, len(sh.pl), rsd[r:r + 1])
+            gd = [to_dev_u16(torch, g, dev) for g in G]
+            z.mta_update(gd, sh.begin, sh.plan, hp_at(t), rsd, W, flags=z.STORE_G, info_out=info, ws=ws)
+            torch.cuda.synchronize()
+            rs = part.copy()
+            oi = oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), rs, r)
+            ni = info.cpu().numpy()
+            assert rel_close(rsd[r].item(), part[r], NORM_TOL)
+            assert rel_close(ni[1], oi.norm, NORM_TOL)
+            assert bool(ni[2:4].view(np.int32)[1]) == oi.clip and ni[2:3].view(np.float32)[0] == oi.coef
+        master, m, v, p = sh.gather()
+        what = f"bucketed rank {r}"
+        assert_f32_equal(master, o.master, "master " + what)
+        assert_f32_equal(m, o.m, "m " + what)
+        assert_f32_equal(v, o.v, "v " + what)
+        assert_bf16_equal(p, o.param, "param " + what)
+    with pytest.raises(z.Zero1Error):
+        z.mta_reduce_range(gd, sh.plan, 5, 3, parts[:1], ws=ws)
+    with pytest.raises(z.Zero1Error):
+        z.mta_reduce_range(gd, sh.plan, 0, 10, parts[:1], flags=z.RECOMPUTE_G, ws=ws)

@@ -101,6 +101,10 @@ def lib():
         L.zero1_mta_update.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                        P, i32, u32, P, P, szt, P]
         L.zero1_mta_update.restype = i32
+        L.zero1_mta_reduce_range.argtypes = [P, i32, ctypes.POINTER(Plan), i64, i64, P, u32, P, szt, P]
+        L.zero1_mta_reduce_range.restype = i32
+        L.zero1_partials_sum.argtypes = [P, i32, P, P]
+        L.zero1_partials_sum.restype = i32
         L.zero1_mta_design.argtypes = [P, i32, i64, ctypes.POINTER(Plan), u32]
         L.zero1_mta_design.restype = i32
         L.zero1_mta_step.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
@@ -254,6 +258,19 @@ def mta_update(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, flag
     _check(lib().zero1_mta_update(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
                                   ctypes.byref(h), _addr(rank_sumsq), n_ranks, flags,
                                   _addr(info_out), w, wb, _stream(stream)))
+
+
+def mta_reduce_range(grads, plan: Plan, lo: int, hi: int, sumsq_out, flags: int = STORE_G, ws=None,
+                     ws_bytes=None, stream=None):
+    """grads[w] addresses replica w's gradient of shard element lo."""
+    arr = _ptrs(grads)
+    w, wb = _ws(ws, ws_bytes)
+    _check(lib().zero1_mta_reduce_range(ctypes.cast(arr, P), len(grads), ctypes.byref(plan), lo, hi,
+                                        _addr(sumsq_out), flags, w, wb, _stream(stream)))
+
+
+def partials_sum(parts, n: int, sum_out, stream=None):
+    _check(lib().zero1_partials_sum(_addr(parts), n, _addr(sum_out), _stream(stream)))
 
 
 def mta_design(grads, begin: int, plan: Plan, flags: int = 0) -> int:

@@ -589,6 +589,47 @@ zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin
     return finish(s);
 }
 
+zero1_status zero1_mta_reduce_range(const uint16_t* const* grads, int W, const zero1_plan* plan, int64_t lo,
+                                   int64_t hi, double* sumsq_out, uint32_t flags, void* ws, size_t ws_bytes,
+                                   void* stream)
+{
+    if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_reduce_range")) return fs;
+    zero1_status st;
+    if (!plan || !plan->table) return fail(ZERO1_EINVAL, "plan is NULL or has no table");
+    if (!sumsq_out) return fail(ZERO1_EINVAL, "sumsq_out is NULL");
+    if (lo < 0 || hi < lo || hi > plan->shard_len)
+        return fail(ZERO1_EINVAL, "range [%lld, %lld) is not inside the shard [0, %lld)", (long long)lo,
+                    (long long)hi, (long long)plan->shard_len);
+    if (flags & (ZERO1_RECOMPUTE_G | ZERO1_ONCHIP))
+        return fail(ZERO1_EINVAL, "zero1_mta_reduce_range stores g: it pairs with ZERO1_STORE_G only");
+    Reduce r;
+    bool vec = false;
+    if ((st = check_grads(grads, W, 0, hi - lo, r, flags, vec))) return st;
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+    Ws w;
+    if ((st = carve(ws, ws_bytes, zero1_mta_workspace_bytes(plan, W, ZERO1_STORE_G), true, w))) return st;
+    float* g = w.g + lo;
+    if (reinterpret_cast<uintptr_t>(g) % 16) vec = false;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Shape sh = reduce_shape(tiles(hi - lo, vec), d);
+    if (hi > lo) Z1_HIP(launch_reduce(r, hi - lo, vec, g, w.partials, sh.grid, sh.split, s));
+    Z1_HIP(launch_finalize(w.partials, hi > lo ? sh.grid : 0, sumsq_out, s));
+    return finish(s);
+}
+
+zero1_status zero1_partials_sum(const double* parts, int n, double* sum_out, void* stream)
+{
+    if (n < 0 || n > kMaxPartials) return fail(ZERO1_EINVAL, "n=%d must be in [0, %d]", n, kMaxPartials);
+    if ((!parts && n > 0) || !sum_out) return fail(ZERO1_EINVAL, "parts or sum_out is NULL");
+    zero1_status st;
+    DevInfo d;
+    if ((st = current_device(d))) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Z1_HIP(launch_finalize(parts, n, sum_out, s));
+    return finish(s);
+}
+
 zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
                               const zero1_hparams* hp, const double* rank_sumsq, int n_ranks, uint32_t flags,
                               zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
