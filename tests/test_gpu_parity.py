@@ -584,3 +584,48 @@ def test_bucketed_reduction_matches_oracle_and_mta_step(env):
         z.mta_reduce_range(gd, sh.plan, 5, 3, parts[:1], ws=ws)
     with pytest.raises(z.Zero1Error):
         z.mta_reduce_range(gd, sh.plan, 0, 10, parts[:1], flags=z.RECOMPUTE_G, ws=ws)
+
+
+@pytest.mark.parametrize("W", [127, 128])
+def test_shard_reduce_widest(env, W):
+    """The widest replica count the library takes (128) and an odd one next to
+    it (127: the IEEE-division average), over ragged lengths and a misaligned
+    start; the 4-slice load batches run to their ragged last batch."""
+    torch, dev = env
+    ws = ws_tensor(torch, z.workspace_bytes(1 << 16, W), dev)
+    sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+    for length, offset in [(1, 0), (2049, 3), (3 * 2048 + 17, 0)]:
+        N = offset + length + 5
+        G = replicas(3000 + W, length, W, N, 0.5, outlier_pct=2, specials=2)
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        gout = torch.full((length + 4,), float("nan"), dtype=torch.float32, device=dev)
+        z.shard_reduce(gd, offset, length, g_out=gout, sumsq_out=sumsq, ws=ws)
+        torch.cuda.synchronize()
+        exp = oracle.shard_reduce([g[offset:offset + length] for g in G])
+        assert_f32_equal(gout[:length].cpu().numpy(), exp, f"g W={W} len={length} off={offset}")
+        assert np.isnan(gout[length:].cpu().numpy()).all(), "wrote past the end"
+        assert rel_close(float(sumsq.item()), oracle.sumsq(exp), NORM_TOL)
+
+
+def test_mta_widest_replica_count(env):
+    """A whole ragged step at W=128 for two ranks (the slice pointers of all
+    128 replicas travel in the kernel argument)."""
+    torch, dev = env
+    numels = [3000, 1, 70000, 129, 4096]
+    for design in (z.STORE_G, z.RECOMPUTE_G):
+        run_mta_all_ranks(torch, dev, numels, 128, 2, 0xF100, design, False, True,
+                          lambda t: [0.02, 0.3][t % 2], ranks=[0, 77])
+
+
+def test_mta_many_tiny_tensors(env):
+    """A tensor list of 1,500 mostly tiny tensors (1 to 40 elements, a few
+    larger), so most pieces are shorter than a lane group and many shards cut
+    through the middle of one; every rank, both streaming designs."""
+    torch, dev = env
+    rng = np.random.default_rng(0x71A1)
+    numels = [int(x) for x in rng.integers(1, 41, size=1500)]
+    for i in (10, 700, 1499):
+        numels[i] = 5000 + i
+    for design in (z.STORE_G, z.RECOMPUTE_G):
+        run_mta_all_ranks(torch, dev, numels, 3, 2, 0xF200, design, False, True,
+                          lambda t: [0.02, 0.3][t % 2])
