@@ -69,9 +69,10 @@ struct ChunkDesc {
 // Phase 1: g = reduce(slices) over [0, len); optional fp32 store of g and one
 // fp64 partial sum of squares per workgroup (nblocks of them).
 // `split`: 8 splits the units into one contiguous part per XCD, 1 is a plain
-// grid stride (nblocks must be a multiple of split).
+// grid stride (nblocks must be a multiple of split).  g_nt: store g with the
+// non-temporal hint.
 hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out,
-                         double* partials, int nblocks, int split, hipStream_t s);
+                         double* partials, int nblocks, int split, bool g_nt, hipStream_t s);
 // Sum of squares of an fp32 vector, one partial per workgroup.
 hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials,
                         int nblocks, int split, hipStream_t s);

@@ -53,22 +53,20 @@ template <typename T>
 __device__ __forceinline__ void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
 
 // The reduced gradient g (store-g design) is written by one kernel and read
-// back by the next, so unlike every other array its accesses keep the default
-// cache policy: much of the re-read then hits the 256 MB MALL (measured on the
-// GPT-2 small W=8 shard: update kernel 82 -> 75 us).  Z1_G_TEMPORAL=0 gives g
-// the non-temporal hint too.
-#ifndef Z1_G_TEMPORAL
-#define Z1_G_TEMPORAL 1
-#endif
-template <typename T>
+// back by the next.  The update reads it with the default cache policy, so a
+// g that fits in the 256 MB MALL is re-read mostly from there (GPT-2 small
+// W=8 shard: update kernel 82 -> 75 us); the reduce stores it with the default
+// policy for such sizes and with the non-temporal hint (NT) for larger ones,
+// where it cannot stay resident anyway.
+template <bool NT = false, typename T>
 __device__ __forceinline__ T ld_g(const T* p)
 {
-    if constexpr (Z1_G_TEMPORAL) return *p; else return __builtin_nontemporal_load(p);
+    if constexpr (NT) return __builtin_nontemporal_load(p); else return *p;
 }
-template <typename T>
+template <bool NT = false, typename T>
 __device__ __forceinline__ void st_g(T* p, T v)
 {
-    if constexpr (Z1_G_TEMPORAL) *p = v; else __builtin_nontemporal_store(v, p);
+    if constexpr (NT) __builtin_nontemporal_store(v, p); else *p = v;
 }
 
 // Offset of this lane's first quad inside a tile (the second is 256 further).
@@ -141,13 +139,14 @@ __device__ __forceinline__ void ld8_f32(const float* p, float (&x)[8])
     x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void st8_g(float* p, const float (&x)[8])
 {
     const int a = quad_a();
     const f32x4 u = {x[0], x[1], x[2], x[3]};
     const f32x4 w = {x[4], x[5], x[6], x[7]};
-    st_g(reinterpret_cast<f32x4*>(p + a), u);
-    st_g(reinterpret_cast<f32x4*>(p + a + 256), w);
+    st_g<NT>(reinterpret_cast<f32x4*>(p + a), u);
+    st_g<NT>(reinterpret_cast<f32x4*>(p + a + 256), w);
 }
 
 __device__ __forceinline__ void ld8_g(const float* p, float (&x)[8])
@@ -181,25 +180,79 @@ __device__ __forceinline__ float average(const Reduce& r, float s)
     return s;
 }
 
-// This lane's 8 reduced values of the tile at shard index e (vector path).
-__device__ __forceinline__ void reduce8(const Reduce& r, int64_t e, float (&s)[8])
+// One slice's share of a tile for this lane, as loaded: two 8-byte words of
+// four bf16 each (quad a, quad a+256).  Kept packed until the add so that a
+// batch of eight slices holds 32 registers, not 64.
+struct Raw {
+    u32x2 a, b;
+};
+
+__device__ __forceinline__ Raw ld_raw(const uint16_t* p)
 {
-    ld8_bf16(r.gp.p[0] + e, s);
-    for (int w0 = 1; w0 < r.W; w0 += 4) {
-        // issue up to four slices' loads before the first dependent add
-        float x[4][8];
+    const int a = quad_a();
+    return Raw{ld_nt(reinterpret_cast<const u32x2*>(p + a)), ld_nt(reinterpret_cast<const u32x2*>(p + a + 256))};
+}
+
+__device__ __forceinline__ void raw_init(float (&s)[8], const Raw& x)
+{
+    s[0] = bf16_lo(x.a.x); s[1] = bf16_hi(x.a.x); s[2] = bf16_lo(x.a.y); s[3] = bf16_hi(x.a.y);
+    s[4] = bf16_lo(x.b.x); s[5] = bf16_hi(x.b.x); s[6] = bf16_lo(x.b.y); s[7] = bf16_hi(x.b.y);
+}
+
+__device__ __forceinline__ void raw_add(float (&s)[8], const Raw& x)
+{
+    s[0] = s[0] + bf16_lo(x.a.x); s[1] = s[1] + bf16_hi(x.a.x);
+    s[2] = s[2] + bf16_lo(x.a.y); s[3] = s[3] + bf16_hi(x.a.y);
+    s[4] = s[4] + bf16_lo(x.b.x); s[5] = s[5] + bf16_hi(x.b.x);
+    s[6] = s[6] + bf16_lo(x.b.y); s[7] = s[7] + bf16_hi(x.b.y);
+}
+
+// Slices [w0, w0+B) of the tile at e: all B loads are issued before the first
+// add.  The first batch starts the sum (s = G_0) and runs mid() right after
+// its loads are issued: the caller's stores placed there leave the memory
+// queue behind this tile's loads, so waiting for the loads does not also wait
+// for the stores (loads and stores retire through one in-order counter).
+template <int B, bool FIRST, typename Mid>
+__device__ __forceinline__ void reduce_batch(const Reduce& r, int w0, int64_t e, float (&s)[8], Mid& mid)
+{
+    Raw x[B];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (w0 + k < r.W) ld8_bf16(r.gp.p[w0 + k] + e, x[k]);
+    for (int k = 0; k < B; ++k) x[k] = ld_raw(r.gp.p[w0 + k] + e);
+    if constexpr (FIRST) mid();
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (w0 + k < r.W) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s[j] = s[j] + x[k][j];
-            }
+    for (int k = 0; k < B; ++k) {
+        if (FIRST && k == 0) raw_init(s, x[0]);
+        else raw_add(s, x[k]);
     }
+}
+
+// This lane's 8 reduced values of the tile at shard index e (vector path):
+// s = G_0 + G_1 + ... + G_{W-1} in rank order, in batches of eight slices,
+// then one of four, two, then single slices; then the average.
+template <typename Mid>
+__device__ __forceinline__ void reduce8(const Reduce& r, int64_t e, float (&s)[8], Mid mid)
+{
+    int w0;
+    if (r.W >= 8) {
+        reduce_batch<8, true>(r, 0, e, s, mid);
+        for (w0 = 8; w0 + 8 <= r.W; w0 += 8) reduce_batch<8, false>(r, w0, e, s, mid);
+    } else if (r.W >= 4) {
+        reduce_batch<4, true>(r, 0, e, s, mid);
+        w0 = 4;
+    } else {
+        reduce_batch<1, true>(r, 0, e, s, mid);
+        w0 = 1;
+    }
+    if (w0 + 4 <= r.W) { reduce_batch<4, false>(r, w0, e, s, mid); w0 += 4; }
+    if (w0 + 2 <= r.W) { reduce_batch<2, false>(r, w0, e, s, mid); w0 += 2; }
+    if (w0 < r.W) reduce_batch<1, false>(r, w0, e, s, mid);
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[j] = average(r, s[j]);
+}
+
+__device__ __forceinline__ void reduce8(const Reduce& r, int64_t e, float (&s)[8])
+{
+    reduce8(r, e, s, [] {});
 }
 
 __device__ __forceinline__ float reduce1(const Reduce& r, int64_t e)
@@ -232,29 +285,49 @@ __device__ __forceinline__ double block_sum(double x)
 }
 
 // ------------------------------------------------------------- phase 1
-template <bool VEC, bool STORE, bool NORM>
+// W-slice reduce over the workgroup's tiles; optionally stores g (GNT: with
+// the non-temporal hint, for g larger than the MALL) and accumulates this
+// lane's fp64 sum of squares.  Full tiles run a software pipeline: tile t's g
+// is stored only after tile t+step's loads are issued.  A ragged last tile
+// takes the element path.
+template <bool VEC, bool STORE, bool NORM, bool GNT>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len, float* __restrict__ g_out,
                                                           double* __restrict__ partials, int split)
 {
     double acc = 0.0;
     const int64_t ntiles = (len + kTile - 1) / kTile;
     const Units u = xcd_units(ntiles, split);
-    for (int64_t t = u.lo; t < u.hi; t += u.step) {
-        const int64_t base = t * kTile;
-        if (VEC && base + kTile <= len) {
+    int64_t t = u.lo;
+    const int64_t full_end = VEC ? (u.hi < len / kTile ? u.hi : len / kTile) : u.lo;
+    if (VEC && t < full_end) {
+        float sp[8];                // the previous tile's g, stored after the next tile's loads
+        int64_t tp = t;
+        reduce8(r, t * kTile, sp);
+        if constexpr (NORM) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc = fma((double)sp[j], (double)sp[j], acc);
+        }
+        for (t += u.step; t < full_end; t += u.step) {
             float s[8];
-            reduce8(r, base, s);
-            if constexpr (STORE) st8_g(g_out + base, s);
+            reduce8(r, t * kTile, s, [&] {
+                if constexpr (STORE) st8_g<GNT>(g_out + tp * kTile, sp);
+            });
             if constexpr (NORM) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc = fma((double)s[j], (double)s[j], acc);
             }
-        } else {
-            for (int64_t e = base + threadIdx.x; e < base + kTile && e < len; e += kThreads) {
-                const float x = reduce1(r, e);
-                if constexpr (STORE) st_g(g_out + e, x);
-                if constexpr (NORM) acc = fma((double)x, (double)x, acc);
-            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sp[j] = s[j];
+            tp = t;
+        }
+        if constexpr (STORE) st8_g<GNT>(g_out + tp * kTile, sp);
+    }
+    for (; t < u.hi; t += u.step) {
+        const int64_t base = t * kTile;
+        for (int64_t e = base + threadIdx.x; e < base + kTile && e < len; e += kThreads) {
+            const float x = reduce1(r, e);
+            if constexpr (STORE) st_g<GNT>(g_out + e, x);
+            if constexpr (NORM) acc = fma((double)x, (double)x, acc);
         }
     }
     if constexpr (NORM) {
@@ -631,20 +704,27 @@ __global__ __launch_bounds__(kThreads, MINW) void onchip_step_kernel(Reduce r, c
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, double* partials,
-                         int nblocks, int split, hipStream_t s)
+                         int nblocks, int split, bool g_nt, hipStream_t s)
 {
     const dim3 grid(nblocks), block(kThreads);
     const bool store = g_out != nullptr, norm = partials != nullptr;
-#define Z1_REDUCE(V, ST, NO) hipLaunchKernelGGL((reduce_kernel<V, ST, NO>), grid, block, 0, s, r, len, g_out, partials, split)
-    if (vec) {
-        if (store && norm) Z1_REDUCE(true, true, true);
-        else if (store) Z1_REDUCE(true, true, false);
-        else Z1_REDUCE(true, false, true);
-    } else {
-        if (store && norm) Z1_REDUCE(false, true, true);
-        else if (store) Z1_REDUCE(false, true, false);
-        else Z1_REDUCE(false, false, true);
-    }
+#define Z1_REDUCE(V, ST, NO, NT) \
+    hipLaunchKernelGGL((reduce_kernel<V, ST, NO, NT>), grid, block, 0, s, r, len, g_out, partials, split)
+#define Z1_REDUCE_V(V)                                                  \
+    do {                                                                \
+        if (store && norm) {                                            \
+            if (g_nt) Z1_REDUCE(V, true, true, true);                   \
+            else Z1_REDUCE(V, true, true, false);                       \
+        } else if (store) {                                             \
+            if (g_nt) Z1_REDUCE(V, true, false, true);                  \
+            else Z1_REDUCE(V, true, false, false);                      \
+        } else {                                                        \
+            Z1_REDUCE(V, false, true, false);                           \
+        }                                                               \
+    } while (0)
+    if (vec) Z1_REDUCE_V(true);
+    else Z1_REDUCE_V(false);
+#undef Z1_REDUCE_V
 #undef Z1_REDUCE
     return hipGetLastError();
 }
