@@ -12,6 +12,11 @@ parameters) cut into W=8 ZeRO-1 shards; rank 4's 15,554,976-parameter shard
 timed region.  The other ranks' partial sums of squares are computed once
 before timing (they are what a multi-GPU run would exchange mid-step).
 
+Memory: by default every array of the step sits in one allocation laid out by
+zero1_arena_plan (the update's five streams 24 GiB apart; HBM serves them
+faster than arrays packed together); --layout packed allocates each array on
+its own.
+
 Prints ONE JSON line.  Metric: shard parameters updated per second; the
 algorithmic HBM traffic is (2W+26) bytes per parameter (W bf16 gradient reads,
 fp32 master/m/v read + write, bf16 parameter write).
@@ -59,7 +64,12 @@ class Copy:
     that consecutive steps do not find each other's data in the 256 MB MALL)."""
 
 
-def setup(torch, cfg, design_flags, n_copies, dev):
+def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
+    """Every array of n_copies independent copies of one rank's step, resident
+    in HBM.  layout "arena": one allocation laid out by zero1_arena_plan (the
+    update's five streams 24 GiB apart, the gradient buffers packed after
+    them); copy c sits c * delta bytes after copy 0, inside copy 0's gaps.
+    layout "packed": one torch allocation per array."""
     import synth
     import zero_sharded_mixed_zero1_amd as z
 
@@ -71,38 +81,80 @@ def setup(torch, cfg, design_flags, n_copies, dev):
     offsets = [0]
     for n in numels:
         offsets.append(offsets[-1] + n)
+    first, last = pieces_l[0][0], pieces_l[-1][0]
+    p_lo, p_hi = offsets[first], offsets[last + 1]      # the tensors the shard touches
+    grad_elems, grad_off = (N, begin) if cfg.all_replicas_resident else (S, 0)
+    mvdt = torch.int16 if cfg.mv_bf16 else torch.float32
+    mv_flag = z.MV_BF16 if cfg.mv_bf16 else 0
+    arena = None
+    info = {"layout": layout}
+    if layout == "arena":
+        free, _ = torch.cuda.mem_get_info(dev)
+        cap = max(0, free - (8 << 30))
+        L = z.arena_plan(S, W, grad_elems, grad_off, p_hi - p_lo, begin - p_lo,
+                         flags=mv_flag | (design_flags & (z.STORE_G | z.RECOMPUTE_G)), capacity=cap)
+        unit = 2 << 20
+        # copy c is copy 0 shifted by c * delta: delta clears the largest spaced
+        # array and the whole region from the parameter buffer to the end
+        extents = [L.ws_bytes, 4 * S, (2 if cfg.mv_bf16 else 4) * S]
+        delta = (max(extents + [L.total_bytes - L.params]) + unit - 1) // unit * unit
+        total = L.total_bytes + (n_copies - 1) * delta
+        if n_copies > 1 and delta * (n_copies - 1) + max(extents) + 2 * (begin - p_lo) > L.spacing:
+            raise SystemExit("arena: the copies do not fit in the gaps; use --rotate 1 or --layout packed")
+        arena = torch.empty(total, dtype=torch.uint8, device=dev)
+        info.update(arena_bytes=total, spacing_gib=L.spacing / (1 << 30))
+        spans = []
+
+        def view(off, n, dt):
+            nb = n * torch.empty((), dtype=dt).element_size()
+            spans.append((off, off + nb))
+            return arena[off:off + nb].view(dt)
     copies = []
     for c in range(n_copies):
         cp = Copy()
+        if layout == "arena":
+            sh = c * delta
+            bufs = [view(sh + L.grads[w], grad_elems, torch.int16) for w in range(W)]
+            cp.master = view(sh + L.master, S, torch.float32)
+            cp.m = view(sh + L.m, S, mvdt)
+            cp.v = view(sh + L.v, S, mvdt)
+            cp.params = view(sh + L.params, p_hi - p_lo, torch.int16)
+            cp.ws = view(sh + L.ws, L.ws_bytes, torch.uint8)
+        else:
+            bufs = [torch.empty(grad_elems, dtype=torch.int16, device=dev) for _ in range(W)]
+            cp.master = torch.empty(S, dtype=torch.float32, device=dev)
+            cp.m = torch.empty(S, dtype=mvdt, device=dev)
+            cp.v = torch.empty(S, dtype=mvdt, device=dev)
+            cp.params = torch.empty(p_hi - p_lo, dtype=torch.int16, device=dev)
+            cp.ws = None
+        for w, t in enumerate(bufs):
+            synth.fill_bf16_(t, synth.grad_key(cfg.seed, 1, w), begin - grad_off, cfg.sigma, cfg.outlier_pct)
         if cfg.all_replicas_resident:
             # every replica's full flat gradient is resident; the step reads rank's slice
-            cp.full = [torch.empty(N, dtype=torch.int16, device=dev) for _ in range(W)]
-            for w, t in enumerate(cp.full):
-                synth.fill_bf16_(t, synth.grad_key(cfg.seed, 1, w), 0, cfg.sigma, cfg.outlier_pct)
-            cp.grads = cp.full
+            cp.full = bufs
             cp.begin = begin
         else:
             # only this rank's W slices exist (their global flat indices start at begin)
-            cp.grads = [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(W)]
-            for w, t in enumerate(cp.grads):
-                synth.fill_bf16_(t, synth.grad_key(cfg.seed, 1, w), begin, cfg.sigma, cfg.outlier_pct)
             cp.begin = 0
-        cp.master = torch.empty(S, dtype=torch.float32, device=dev)
+        cp.grads = bufs
         synth.fill_f32_(cp.master, synth.master_key(cfg.seed), begin, cfg.master_sigma)
-        mvdt = torch.int16 if cfg.mv_bf16 else torch.float32
-        cp.m = torch.zeros(S, dtype=mvdt, device=dev)
-        cp.v = torch.zeros(S, dtype=mvdt, device=dev)
-        # the whole model's bf16 parameters, one buffer per tensor list (pieces point inside)
-        first, last = pieces_l[0][0], pieces_l[-1][0]
-        lo, hi = offsets[first], offsets[last + 1]
-        cp.params = torch.zeros(hi - lo, dtype=torch.int16, device=dev)
-        pieces = [(n, so, cp.params[offsets[ti] - lo + off:], cp.master[so:], cp.m[so:], cp.v[so:])
+        cp.m.zero_()
+        cp.v.zero_()
+        cp.params.zero_()
+        # the model's bf16 parameters of the tensors the shard touches (pieces point inside)
+        pieces = [(n, so, cp.params[offsets[ti] - p_lo + off:], cp.master[so:], cp.m[so:], cp.v[so:])
                   for ti, off, so, n in pieces_l]
         cp.table = torch.empty(max(256, z.mta_table_bytes(pieces)), dtype=torch.uint8, device=dev)
-        cp.plan = z.mta_plan(pieces, cp.table, flags=z.MV_BF16 if cfg.mv_bf16 else 0)
-        cp.ws = torch.empty(z.mta_workspace_bytes(cp.plan, W, design_flags), dtype=torch.uint8, device=dev)
+        cp.plan = z.mta_plan(pieces, cp.table, flags=mv_flag)
+        if cp.ws is None or cp.ws.numel() < z.mta_workspace_bytes(cp.plan, W, design_flags):
+            cp.ws = torch.empty(z.mta_workspace_bytes(cp.plan, W, design_flags), dtype=torch.uint8, device=dev)
         cp.rsd = torch.zeros(W, dtype=torch.float64, device=dev)
         copies.append(cp)
+    if arena is not None:   # no two arrays of any copy overlap (checked before any step runs)
+        spans.sort()
+        for (a0, b0), (a1, b1) in zip(spans, spans[1:]):
+            if b0 > a1:
+                raise SystemExit(f"arena: arrays overlap at byte {a1}")
     # the other ranks' partial sums of squares (C1/C2: all replicas resident -> true global norm;
     # otherwise only this rank's slices exist and the other partials are 0: shard-local norm)
     if cfg.all_replicas_resident:
@@ -115,7 +167,7 @@ def setup(torch, cfg, design_flags, n_copies, dev):
         for cp in copies[1:]:
             cp.rsd.copy_(c0.rsd)
     torch.cuda.synchronize()
-    return dict(W=W, rank=rank, N=N, S=S, begin=begin, pieces=len(pieces_l), copies=copies)
+    return dict(W=W, rank=rank, N=N, S=S, begin=begin, pieces=len(pieces_l), copies=copies, info=info)
 
 
 def hp(cfg, t):
@@ -322,6 +374,8 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--design", choices=["auto", "onchip", "store", "recompute"], default="auto")
     ap.add_argument("--rotate", type=int, default=0, help="independent copies to rotate (0: auto)")
+    ap.add_argument("--layout", choices=["arena", "packed"], default="arena",
+                    help="arena: arrays placed by zero1_arena_plan; packed: one torch allocation each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
@@ -352,7 +406,7 @@ def main():
     store_g = bool(flags & z.STORE_G) or (not (flags & (z.RECOMPUTE_G | z.ONCHIP)) and cfg.W > 4)
     per_copy = cfg.S * (2 * cfg.W + 26 + (4 if store_g else 0))
     n_copies = a.rotate or (2 if per_copy < (1 << 30) else 1)
-    st = setup(torch, cfg, flags, n_copies, dev)
+    st = setup(torch, cfg, flags, n_copies, dev, a.layout)
     S, W = st["S"], st["W"]
     c0 = st["copies"][0]
     design = z.mta_design(c0.grads, c0.begin, c0.plan, flags)
@@ -421,6 +475,7 @@ def main():
             "W": W, "rank": st["rank"], "shard_params": S, "pieces": st["pieces"],
             "bytes_per_param": bpp, "design": design_name,
             "rotated_copies": n_copies, "m_v": "bf16" if cfg.mv_bf16 else "fp32",
+            "memory_layout": st["info"],
         },
         "algorithmic_GBps": value * bpp / 1e9,
         "pct_of_peak_hbm": 100.0 * value * bpp / 1e9 / PEAK_HBM_GBS,

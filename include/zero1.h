@@ -310,6 +310,60 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
                             uint32_t flags, zero1_norm_info* info_out,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- arena
+ * Placement of one rank's optimizer arrays inside one device allocation (the
+ * arena).  On MI355X the HBM throughput of a kernel that streams several
+ * arrays at once depends on how far apart the arrays are: the update's five
+ * streams (the reduced gradient g -- or gradient slice 0 when g is recomputed
+ * --, master, m, v and the shard's bf16 parameters) run at about 6.2 TB/s when
+ * they are 24 GiB or more apart and at about 5.1 TB/s when packed within
+ * 12 GiB (Llama-7B/8 shard; 6.7 vs 6.2 TB/s at the GPT-2-small/8 shard).  The
+ * planner puts those five at one spacing D (24 GiB, or more when an array is
+ * larger, or less when `capacity` is short) and packs the remaining gradient
+ * buffers after the parameter buffer.  The gaps between the spaced arrays are
+ * not used by the library: the caller may place its other tensors there.
+ *
+ * Request: shard_len S >= 1; W in 1..ZERO1_MAX_W gradient buffers of
+ * grad_elems bf16 each, this rank's shard starting at element grad_offset of
+ * each (grad_offset = 0, grad_elems = S for buffers that hold only the shard;
+ * the shard's begin and N for full replicas); the flat bf16 parameter buffer
+ * of param_elems elements with the shard starting at param_offset; flags:
+ * ZERO1_MV_BF16 (2-byte m, v) and the design (ZERO1_STORE_G, ZERO1_RECOMPUTE_G,
+ * or neither for the one zero1_mta_step picks; ZERO1_ONCHIP is planned like
+ * RECOMPUTE_G); capacity: the largest arena the caller can allocate.
+ *
+ * Layout (byte offsets from the arena base, which must be 2 MiB aligned): the
+ * workspace (ws_bytes = zero1_mta_workspace_bytes for that design; holds g),
+ * master, m, v, the parameter buffer and each gradient buffer.  Every spaced
+ * array's shard range starts on a 2 MiB boundary; the other buffers start on
+ * 2 MiB boundaries.  Arrays never overlap; total_bytes <= capacity.
+ * ZERO1_EINVAL when the request is invalid or even the packed layout (spacing
+ * = the smallest that keeps the arrays apart) exceeds capacity.  Host only:
+ * no device call. */
+typedef struct zero1_arena_request {
+    int64_t shard_len;
+    int W;
+    int64_t grad_elems;
+    int64_t grad_offset;
+    int64_t param_elems;
+    int64_t param_offset;
+    uint32_t flags;
+    size_t capacity;
+} zero1_arena_request;
+
+typedef struct zero1_arena_layout {
+    size_t total_bytes;
+    size_t spacing;            /* D actually used */
+    size_t ws, ws_bytes;
+    size_t master, m, v;
+    size_t params;             /* start of the parameter buffer (element 0) */
+    size_t grads[ZERO1_MAX_W]; /* start of each gradient buffer (element 0) */
+} zero1_arena_layout;
+
+#define ZERO1_ARENA_SPACING ((size_t)24 << 30)   /* preferred spacing D */
+
+zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -196,3 +196,74 @@ def test_bucketed_reduction_rejects_bad_arguments():
     assert "n=" in _einval(lambda: z.partials_sum(FAKE, -1, FAKE, stream=0))
     assert "n=" in _einval(lambda: z.partials_sum(FAKE, 8193, FAKE, stream=0))
     assert "NULL" in _einval(lambda: z.partials_sum(FAKE, 4, 0, stream=0))
+
+
+# ---------------------------------------------------------------- arena planner
+GiB = 1 << 30
+UNIT = 2 << 20
+
+
+def _arena_intervals(L, req_W, S, grad_elems, param_elems, mvb, store_g):
+    iv = [("ws", L.ws, L.ws + L.ws_bytes), ("master", L.master, L.master + 4 * S),
+          ("m", L.m, L.m + mvb * S), ("v", L.v, L.v + mvb * S),
+          ("params", L.params, L.params + 2 * param_elems)]
+    iv += [(f"grads[{w}]", L.grads[w], L.grads[w] + 2 * grad_elems) for w in range(req_W)]
+    return iv
+
+
+@pytest.mark.parametrize("S,W,ge,go,pe,po,flags", [
+    (15554976, 8, 124439808, 4 * 15554976, 124439808, 4 * 15554976, 0),          # GPT-2 small, full replicas
+    (842301952, 8, 842301952, 0, 6738415616, 3 * 842301952, 0),                   # Llama-7B/8 rank 3
+    (117187500, 64, 117187500, 0, 7_500_000_000, 0, 0),                            # 7.5e9/64 rank 0
+    (7_000_000_000, 1, 7_000_000_000, 0, 7_000_000_000, 0, z.MV_BF16),             # 7e9 W=1 bf16 m,v
+    (262144, 4, 1 << 20, 0, 1 << 20, 0, z.RECOMPUTE_G),                            # 2^20 W=4, rank 0
+    (1000, 3, 5000, 1234, 7000, 99, z.STORE_G),
+    (1000, 3, 5000, 1234, 7000, 99, z.RECOMPUTE_G | z.MV_BF16),
+])
+def test_arena_plan_layout(S, W, ge, go, pe, po, flags):
+    for cap in (1 << 62, None):
+        if cap is None:   # a capacity that forces a smaller spacing
+            full = z.arena_plan(S, W, ge, go, pe, po, flags)
+            cap = full.total_bytes - 4 * (full.spacing // 3)
+            if full.spacing > 24 * GiB:
+                # the arrays themselves set the spacing: nothing smaller fits
+                assert "packed layout" in _einval(lambda: z.arena_plan(S, W, ge, go, pe, po, flags, capacity=cap))
+                continue
+        L = z.arena_plan(S, W, ge, go, pe, po, flags, capacity=cap)
+        store_g = bool(flags & z.STORE_G) or (not (flags & z.RECOMPUTE_G) and W > 4)
+        mvb = 2 if flags & z.MV_BF16 else 4
+        assert L.total_bytes <= cap
+        assert L.ws_bytes == z.lib().zero1_workspace_bytes(S, W, z.STORE_G if store_g else 0)
+        iv = _arena_intervals(L, W, S, ge, pe, mvb, store_g)
+        for name, a, b in iv:
+            assert 0 <= a < b <= L.total_bytes, name
+        iv.sort(key=lambda x: x[1])
+        for (n1, a1, b1), (n2, a2, b2) in zip(iv, iv[1:]):
+            assert b1 <= a2, f"{n1} overlaps {n2}"
+        # the five spaced shard starts sit at base + k D, on 2 MiB boundaries
+        base = L.ws if store_g else L.grads[0] + 2 * go
+        starts = [base, L.master, L.m, L.v, L.params + 2 * po]
+        assert all(x % UNIT == 0 for x in starts) and L.spacing % UNIT == 0
+        assert starts == [base + k * L.spacing for k in range(5)]
+        if cap == 1 << 62:
+            assert L.spacing >= 24 * GiB
+        else:
+            assert L.spacing < 24 * GiB
+        # the remaining buffers start on 2 MiB boundaries
+        for w in range(0 if store_g else 1, W):
+            assert L.grads[w] % UNIT == 0
+        if not store_g:
+            assert L.ws % UNIT == 0
+
+
+def test_arena_plan_rejects():
+    msg = _einval(lambda: z.arena_plan(0, 8, 10, 0, 10, 0))
+    assert "shard_len" in msg
+    assert "W=0" in _einval(lambda: z.arena_plan(10, 0, 10, 0, 10, 0))
+    assert "W=129" in _einval(lambda: z.arena_plan(10, 129, 10, 0, 10, 0))
+    assert "gradient buffers" in _einval(lambda: z.arena_plan(10, 2, 15, 6, 10, 0))
+    assert "parameter buffer" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 19, 10))
+    assert "exclusive" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, z.STORE_G | z.RECOMPUTE_G))
+    assert "do not apply" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, z.DECAY_FIRST))
+    assert "unknown" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, 1 << 24))
+    assert "capacity" in _einval(lambda: z.arena_plan(1 << 20, 8, 1 << 20, 0, 1 << 20, 0, 0, capacity=1 << 20))

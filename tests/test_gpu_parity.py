@@ -629,3 +629,66 @@ def test_mta_many_tiny_tensors(env):
     for design in (z.STORE_G, z.RECOMPUTE_G):
         run_mta_all_ranks(torch, dev, numels, 3, 2, 0xF200, design, False, True,
                           lambda t: [0.02, 0.3][t % 2])
+
+
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
+def test_mta_step_in_planned_arena(env, design):
+    """Every array of one rank placed in one allocation by zero1_arena_plan
+    (the spaced arrays 24 GiB apart, full replica gradients packed after the
+    parameter buffer): two steps, bit-exact against the oracle, and nothing
+    outside the arrays is written."""
+    torch, dev = env
+    numels = [3000, 17, 5000, 65536 + 3, 8192 * 2 + 1]
+    N, W, r = sum(numels), 4, 1
+    begin, S = z.shard_range(N, W, r)
+    L = z.arena_plan(S, W, N, begin, N, begin, flags=design)
+    assert L.spacing >= 24 << 30
+    arena = torch.empty(L.total_bytes, dtype=torch.uint8, device=dev)
+    guard = 4096   # sentinel bytes after every array
+
+    def view(off, n, dt):
+        nb = n * torch.empty((), dtype=dt).element_size()
+        arena[off + nb:off + nb + guard].fill_(0xA5)
+        return arena[off:off + nb].view(dt)
+    grads = [arena[L.grads[w]:L.grads[w] + 2 * N].view(torch.int16) for w in range(W)]
+    master = view(L.master, S, torch.float32)
+    m = view(L.m, S, torch.float32)
+    v = view(L.v, S, torch.float32)
+    params = arena[L.params:L.params + 2 * N].view(torch.int16)
+    ws = (view if design == z.STORE_G else lambda o, n, d: arena[o:o + n].view(d))(L.ws, L.ws_bytes, torch.uint8)
+    master_full = synth.f32(N, synth.master_key(0xF300), 0, 0.02)
+    master.copy_(torch.from_numpy(master_full[begin:begin + S].copy()))
+    m.zero_()
+    v.zero_()
+    params.zero_()
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[begin:begin + S])
+    offs = np.concatenate([[0], np.cumsum(numels)])
+    pieces = [(n, so, params[offs[ti] + off:], master[so:], m[so:], v[so:])
+              for ti, off, so, n in z.shard_pieces(numels, begin, begin + S)]
+    table = torch.empty(max(256, z.mta_table_bytes(pieces)), dtype=torch.uint8, device=dev)
+    plan = z.mta_plan(pieces, table)
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    for t in (1, 2):
+        G = replicas(0xF300, t, W, N, [0.02, 0.3][t - 1], outlier_pct=1)
+        for w in range(W):
+            grads[w].copy_(torch.from_numpy(G[w].view(np.int16)))
+        part = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                         for b, n in (z.shard_range(N, W, q) for q in range(W))])
+        rsd.copy_(torch.from_numpy(part))
+        z.mta_step(grads, begin, plan, hp_at(t), rsd, W, r, flags=design, ws=ws)
+        torch.cuda.synchronize()
+        oracle.step([g[begin:begin + S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), part.copy(), r)
+    assert_f32_equal(master.cpu().numpy(), o.master, "master in arena")
+    assert_f32_equal(m.cpu().numpy(), o.m, "m in arena")
+    assert_f32_equal(v.cpu().numpy(), o.v, "v in arena")
+    assert_bf16_equal(to_np_u16(params[begin:begin + S]), o.param, "params in arena")
+    # the parameters outside the shard and the guard bands after the spaced
+    # arrays (each followed by a gap) are untouched
+    p_all = to_np_u16(params)
+    assert not p_all[:begin].any() and not p_all[begin + S:].any()
+    spaced = [(L.master, 4 * S), (L.m, 4 * S), (L.v, 4 * S)] + ([(L.ws, L.ws_bytes)] if design == z.STORE_G else [])
+    for off, nb in spaced:
+        assert (arena[off + nb:off + nb + guard] == 0xA5).all(), "wrote past an array"
+    del arena
+    torch.cuda.empty_cache()

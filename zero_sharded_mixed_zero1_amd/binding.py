@@ -62,6 +62,19 @@ class Plan(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("aligned", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class ArenaRequest(ctypes.Structure):
+    _fields_ = [("shard_len", i64), ("W", i32), ("grad_elems", i64), ("grad_offset", i64),
+                ("param_elems", i64), ("param_offset", i64), ("flags", ctypes.c_uint32),
+                ("capacity", ctypes.c_size_t)]
+
+
+class ArenaLayout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_size_t), ("spacing", ctypes.c_size_t),
+                ("ws", ctypes.c_size_t), ("ws_bytes", ctypes.c_size_t),
+                ("master", ctypes.c_size_t), ("m", ctypes.c_size_t), ("v", ctypes.c_size_t),
+                ("params", ctypes.c_size_t), ("grads", ctypes.c_size_t * 128)]
+
+
 _lib = None
 
 
@@ -110,6 +123,8 @@ def lib():
         L.zero1_mta_step.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                      P, i32, i32, u32, P, P, szt, P]
         L.zero1_mta_step.restype = i32
+        L.zero1_arena_plan.argtypes = [ctypes.POINTER(ArenaRequest), ctypes.POINTER(ArenaLayout)]
+        L.zero1_arena_plan.restype = i32
         _lib = L
     return _lib
 
@@ -287,3 +302,12 @@ def mta_step(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, my_ran
     _check(lib().zero1_mta_step(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
                                 ctypes.byref(h), _addr(rank_sumsq), n_ranks, my_rank, flags,
                                 _addr(info_out), w, wb, _stream(stream)))
+
+
+def arena_plan(shard_len: int, W: int, grad_elems: int, grad_offset: int, param_elems: int,
+               param_offset: int, flags: int = 0, capacity: int = 1 << 62) -> ArenaLayout:
+    """Byte offsets of one rank's arrays inside one arena (zero1_arena_plan)."""
+    req = ArenaRequest(shard_len, W, grad_elems, grad_offset, param_elems, param_offset, flags, capacity)
+    out = ArenaLayout()
+    _check(lib().zero1_arena_plan(ctypes.byref(req), ctypes.byref(out)))
+    return out

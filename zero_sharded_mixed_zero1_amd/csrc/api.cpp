@@ -725,4 +725,80 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
     return zero1_mta_update(grads, W, begin, plan, hp, rank_sumsq, n_ranks, flags, info_out, ws, ws_bytes, stream);
 }
 
+zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout* out)
+{
+    if (!req || !out) return fail(ZERO1_EINVAL, "request or layout is NULL");
+    const zero1_arena_request& q = *req;
+    if (zero1_status fs = check_flags(q.flags, ZERO1_MV_BF16 | ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP,
+                                      "zero1_arena_plan"))
+        return fs;
+    const uint32_t designs = q.flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
+    if (designs & (designs - 1))
+        return fail(ZERO1_EINVAL, "ZERO1_STORE_G, ZERO1_RECOMPUTE_G and ZERO1_ONCHIP are exclusive");
+    if (q.shard_len < 1) return fail(ZERO1_EINVAL, "shard_len=%lld must be >= 1", (long long)q.shard_len);
+    if (q.W < 1 || q.W > kMaxW) return fail(ZERO1_EINVAL, "W=%d must be in [1, %d]", q.W, kMaxW);
+    if (q.grad_offset < 0 || q.grad_elems < q.grad_offset + q.shard_len)
+        return fail(ZERO1_EINVAL, "gradient buffers of %lld elements cannot hold the shard at %lld",
+                    (long long)q.grad_elems, (long long)q.grad_offset);
+    if (q.param_offset < 0 || q.param_elems < q.param_offset + q.shard_len)
+        return fail(ZERO1_EINVAL, "the parameter buffer of %lld elements cannot hold the shard at %lld",
+                    (long long)q.param_elems, (long long)q.param_offset);
+    const size_t unit = (size_t)2 << 20;
+    const size_t S = (size_t)q.shard_len;
+    const bool store_g = use_store_g(q.flags, q.W);
+    const size_t mvb = (q.flags & ZERO1_MV_BF16) ? 2 : 4;
+    const size_t ws_bytes = zero1_workspace_bytes(q.shard_len, q.W, store_g ? ZERO1_STORE_G : 0);
+    const size_t grad_bytes = round_up((size_t)q.grad_elems * 2, unit);
+
+    // the five spaced slots: bytes of each buffer before and after its shard start
+    struct Slot { size_t before, after; };
+    const Slot slot[5] = {
+        store_g ? Slot{0, ws_bytes} : Slot{(size_t)q.grad_offset * 2, (size_t)(q.grad_elems - q.grad_offset) * 2},
+        {0, S * 4},
+        {0, S * mvb},
+        {0, S * mvb},
+        {(size_t)q.param_offset * 2, (size_t)(q.param_elems - q.param_offset) * 2},
+    };
+    const size_t base = round_up(slot[0].before, unit);   // shard start of slot 0
+    size_t d_min = 0;
+    for (int k = 0; k < 4; ++k) d_min = std::max(d_min, slot[k].after + slot[k + 1].before);
+    d_min = round_up(d_min, unit);
+    // what follows the parameter buffer: the gradient buffers not spaced, and
+    // the workspace when it is not slot 0
+    size_t tail = (size_t)(store_g ? q.W : q.W - 1) * grad_bytes + (store_g ? 0 : round_up(ws_bytes, unit));
+    const size_t fixed = base + round_up(slot[4].after, unit) + tail;   // everything but 4 D
+    size_t d = std::max(d_min, ZERO1_ARENA_SPACING);
+    if (fixed + 4 * d > q.capacity) {
+        if (q.capacity < fixed + 4 * d_min)
+            return fail(ZERO1_EINVAL, "capacity %zu bytes is below the packed layout's %zu", q.capacity,
+                        fixed + 4 * d_min);
+        d = (q.capacity - fixed) / 4 / unit * unit;
+    }
+    zero1_arena_layout L;
+    std::memset(&L, 0, sizeof L);
+    L.spacing = d;
+    L.ws_bytes = ws_bytes;
+    L.master = base + d;
+    L.m = base + 2 * d;
+    L.v = base + 3 * d;
+    L.params = base + 4 * d - slot[4].before;
+    size_t next = round_up(base + 4 * d + slot[4].after, unit);
+    int w0 = 0;
+    if (store_g) {
+        L.ws = base;
+    } else {
+        L.grads[0] = base - slot[0].before;
+        w0 = 1;
+        L.ws = next;
+        next += round_up(ws_bytes, unit);
+    }
+    for (int w = w0; w < q.W; ++w) {
+        L.grads[w] = next;
+        next += grad_bytes;
+    }
+    L.total_bytes = next;
+    *out = L;
+    return ok();
+}
+
 }  // extern "C"
