@@ -34,7 +34,13 @@
  *     `stream` (a hipStream_t, NULL = the null stream) and nothing synchronizes:
  *     results are ready when the stream reaches them, and a fault inside a kernel
  *     surfaces at the caller's next synchronization.  Setting the environment
- *     variable ZERO1_SYNC_CHECK=1 makes each call synchronize and check (tests).
+ *     variable ZERO1_SYNC_CHECK=1 makes each call synchronize and check (tests;
+ *     on a stream under graph capture it checks the launches only).
+ *   - Graph capture: apart from zero1_mta_plan (a synchronous table upload) and
+ *     the ZERO1_ONCHIP cooperative launch, the entry points only launch kernels
+ *     (no memset, copy or synchronization), so their work can be captured into
+ *     a HIP graph.  The fp32 scalars derived from zero1_hparams -- the step t
+ *     included -- are kernel arguments and are frozen into the graph.
  *   - bf16 values are passed as uint16_t bit patterns; fp32 as float.
  *   - Arguments are validated on the host before anything is launched; a
  *     rejected call launches nothing and returns an error status, with a

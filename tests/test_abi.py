@@ -264,6 +264,7 @@ def test_arena_plan_rejects():
     assert "gradient buffers" in _einval(lambda: z.arena_plan(10, 2, 15, 6, 10, 0))
     assert "parameter buffer" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 19, 10))
     assert "exclusive" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, z.STORE_G | z.RECOMPUTE_G))
-    assert "do not apply" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, z.DECAY_FIRST))
+    # flags that do not concern the layout are ignored
+    assert z.arena_plan(10, 2, 10, 0, 10, 0, z.DECAY_FIRST).total_bytes == z.arena_plan(10, 2, 10, 0, 10, 0).total_bytes
     assert "unknown" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, 1 << 24))
     assert "capacity" in _einval(lambda: z.arena_plan(1 << 20, 8, 1 << 20, 0, 1 << 20, 0, 0, capacity=1 << 20))

@@ -692,3 +692,47 @@ def test_mta_step_in_planned_arena(env, design):
         assert (arena[off + nb:off + nb + guard] == 0xA5).all(), "wrote past an array"
     del arena
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
+def test_mta_step_captured_in_a_graph(env, design):
+    """The step captured into a HIP graph (torch.cuda.graph) and replayed three
+    times, with eager work and synchronizations between the replays, gives
+    bit for bit the state of three eager calls with the same arguments."""
+    torch, dev = env
+    numels, W, r = RAGGED, 4, 2
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF400), 0, 0.02)
+    eager = MtaShard(torch, dev, numels, W, r, master_full)
+    graphed = MtaShard(torch, dev, numels, W, r, master_full)
+    ws_e, ws_g = eager.workspace(design), graphed.workspace(design)
+    G = replicas(0xF400, 1, W, N, 0.3, outlier_pct=1)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    part = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                     for b, n in (z.shard_range(N, W, q) for q in range(W))])
+    rsd_e = torch.from_numpy(part.copy()).to(dev)
+    rsd_g = torch.from_numpy(part.copy()).to(dev)
+    info_e = torch.zeros(4, dtype=torch.float64, device=dev)
+    info_g = torch.zeros(4, dtype=torch.float64, device=dev)
+    hp = hp_at(1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        z.mta_step(gd, eager.begin, graphed.plan, hp, rsd_g, W, r, flags=design, info_out=info_g, ws=ws_g)
+    torch.cuda.synchronize()
+    scratch = torch.ones(1 << 20, device=dev)
+    for k in range(3):
+        z.mta_step(gd, eager.begin, eager.plan, hp, rsd_e, W, r, flags=design, info_out=info_e, ws=ws_e)
+        graph.replay()
+        scratch.mul_(1.0001).add_(1.0)        # eager work between the replays
+        torch.cuda.synchronize()
+        a, b = eager.gather(), graphed.gather()
+        what = f"replay {k} design {design}"
+        assert_f32_equal(b[0], a[0], "master " + what)
+        assert_f32_equal(b[1], a[1], "m " + what)
+        assert_f32_equal(b[2], a[2], "v " + what)
+        assert_bf16_equal(b[3], a[3], "param " + what)
+        assert rsd_g[r].item() == rsd_e[r].item()
+        assert torch.equal(info_g, info_e)
+        assert graphed.untouched_outside()
+    del graph

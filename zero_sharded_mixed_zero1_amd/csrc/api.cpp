@@ -65,7 +65,11 @@ bool sync_check_enabled()
 zero1_status finish(hipStream_t s)
 {
     if (sync_check_enabled()) {
-        Z1_HIP(hipStreamSynchronize(s));
+        // a stream being captured into a graph cannot be synchronized: check
+        // the launches only
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        Z1_HIP(hipStreamIsCapturing(s, &cs));
+        if (cs == hipStreamCaptureStatusNone) Z1_HIP(hipStreamSynchronize(s));
         Z1_HIP(hipGetLastError());
     }
     return ok();
@@ -729,9 +733,7 @@ zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout
 {
     if (!req || !out) return fail(ZERO1_EINVAL, "request or layout is NULL");
     const zero1_arena_request& q = *req;
-    if (zero1_status fs = check_flags(q.flags, ZERO1_MV_BF16 | ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP,
-                                      "zero1_arena_plan"))
-        return fs;
+    if (zero1_status fs = check_flags(q.flags, kAllFlags, "zero1_arena_plan")) return fs;
     const uint32_t designs = q.flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
     if (designs & (designs - 1))
         return fail(ZERO1_EINVAL, "ZERO1_STORE_G, ZERO1_RECOMPUTE_G and ZERO1_ONCHIP are exclusive");
