@@ -40,7 +40,9 @@
  *     the ZERO1_ONCHIP cooperative launch, the entry points only launch kernels
  *     (no memset, copy or synchronization), so their work can be captured into
  *     a HIP graph.  The fp32 scalars derived from zero1_hparams -- the step t
- *     included -- are kernel arguments and are frozen into the graph.
+ *     included -- are kernel arguments and are frozen into the graph, unless
+ *     hp->device_scalars points them at device memory that the caller
+ *     rewrites before each replay (zero1_step_scalars_derive).
  *   - bf16 values are passed as uint16_t bit patterns; fp32 as float.
  *   - Arguments are validated on the host before anything is launched; a
  *     rejected call launches nothing and returns an error status, with a
@@ -69,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ZERO1_ABI_VERSION 1
+#define ZERO1_ABI_VERSION 2
 #define ZERO1_MAX_W 128          /* largest number of replicas per call */
 
 typedef enum zero1_status {
@@ -118,7 +120,33 @@ typedef struct zero1_hparams {
     double weight_decay;    /* >= 0; decay factor 1 - lr*weight_decay           */
     double max_norm;        /* > 0; +inf disables clipping                      */
     int64_t step;           /* t >= 1 (bias correction uses beta^t)             */
+    /* NULL, or the DEVICE address (8-byte aligned) of a zero1_step_scalars
+     * that the kernels read when they run, in place of the values derived
+     * from the fields above (which are then neither validated nor read): for a
+     * step captured into a HIP graph and replayed with a new t or learning
+     * rate each iteration (fill it with zero1_step_scalars_derive and copy it
+     * to the device before each replay). */
+    const void* device_scalars;
 } zero1_hparams;
+
+/* The per-step values every step call derives from zero1_hparams: each fp32
+ * scalar is formed in fp64 and rounded once ("并行训练", mixed precision and
+ * AdamW: step_size = lr*sqrt(1-beta2^t)/(1-beta1^t), decay = 1-lr*weight_decay),
+ * and the clip threshold.  40 bytes. */
+typedef struct zero1_step_scalars {
+    float beta1, beta2;
+    float one_minus_beta1, one_minus_beta2;
+    float eps;
+    float step_size;
+    float decay;
+    float reserved;
+    double max_norm;
+} zero1_step_scalars;
+
+/* Fill *out (host memory) from *hp exactly as the step calls do (its
+ * device_scalars field is ignored).  EINVAL for the same hyper-parameters the
+ * step calls reject. */
+zero1_status zero1_step_scalars_derive(const zero1_hparams* hp, zero1_step_scalars* out);
 
 /* Result of the clip stage, written to device memory by the step calls. */
 typedef struct zero1_norm_info {

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = z.lib()
     for n in names:
         assert hasattr(L, n), f"libzero1.so does not export {n}"
-    assert z.abi_version() == 1
+    assert z.abi_version() == 2
 
 
 def test_oracle_and_synth_libraries_load():
@@ -268,3 +268,30 @@ def test_arena_plan_rejects():
     assert z.arena_plan(10, 2, 10, 0, 10, 0, z.DECAY_FIRST).total_bytes == z.arena_plan(10, 2, 10, 0, 10, 0).total_bytes
     assert "unknown" in _einval(lambda: z.arena_plan(10, 2, 10, 0, 10, 0, 1 << 24))
     assert "capacity" in _einval(lambda: z.arena_plan(1 << 20, 8, 1 << 20, 0, 1 << 20, 0, 0, capacity=1 << 20))
+
+
+# ---------------------------------------------------------------- device step scalars
+def test_step_scalars_derive_matches_the_oracle():
+    """The host derivation of the per-step fp32 scalars (what every step call
+    passes to its kernels, and what a graph replay reads from device memory)
+    equals the oracle's, over a sweep of t, lr and betas."""
+    import oracle
+    for t in (1, 2, 3, 10, 1000, 10 ** 6):
+        for lr, b1, b2, eps, wd in [(1e-3, 0.9, 0.95, 1e-8, 0.1), (3e-4, 0.8, 0.999, 1e-6, 0.0),
+                                    (0.1, 0.0, 0.5, 0.0, 1.0), (6e-4, 0.9, 0.95, 1e-8, 0.01)]:
+            s = z.step_scalars_derive(dict(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd,
+                                           max_norm=0.5, step=t))
+            o = oracle.adamw_scalars(lr, b1, b2, eps, wd, t)
+            got = [s.beta1, s.beta2, s.one_minus_beta1, s.one_minus_beta2, s.eps, s.step_size, s.decay]
+            exp = [o.b1, o.b2, o.a1, o.a2, o.eps, o.sigma, o.delta]
+            assert got == exp, (t, lr, got, exp)
+            assert s.max_norm == 0.5 and s.reserved == 0.0
+    assert "step=0" in _einval(lambda: z.step_scalars_derive(_hp(step=0)))
+    assert "beta1" in _einval(lambda: z.step_scalars_derive(_hp(beta1=1.0)))
+
+
+def test_device_scalars_must_be_aligned():
+    bufs = [FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20)]
+    hp = z.HParams(0, 0, 0, 0, 0, 0, 0, FAKE + 4)
+    assert "aligned" in _einval(lambda: z.adamw_step(FAKE + (4 << 20), None, 0, 100, *bufs, hp,
+                                                     FAKE + (5 << 20), 1, stream=0))

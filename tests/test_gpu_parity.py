@@ -736,3 +736,62 @@ def test_mta_step_captured_in_a_graph(env, design):
         assert torch.equal(info_g, info_e)
         assert graphed.untouched_outside()
     del graph
+
+
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G, z.ONCHIP])
+def test_device_scalars_replay_changes_step_and_lr(env, design):
+    """One step captured with its hyper-parameters in device memory, replayed
+    for t = 1..4 under a changing learning rate (the scalars of each step
+    derived on the host and copied in before its replay), equals four eager
+    calls with host hyper-parameters and the oracle's four steps.  ONCHIP is
+    run eagerly with device scalars (its cooperative launch is not captured)."""
+    torch, dev = env
+    numels, W, r = RAGGED8, 4, 3
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF500), 0, 0.02)
+    eager = MtaShard(torch, dev, numels, W, r, master_full)
+    replay = MtaShard(torch, dev, numels, W, r, master_full)
+    ws_e, ws_g = eager.workspace(design), replay.workspace(design)
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[eager.begin:eager.begin + eager.S])
+    G = replicas(0xF500, 1, W, N, 0.3, outlier_pct=1)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    part = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                     for b, n in (z.shard_range(N, W, q) for q in range(W))])
+    rsd_e = torch.from_numpy(part.copy()).to(dev)
+    rsd_g = torch.from_numpy(part.copy()).to(dev)
+    dev_scal = torch.zeros(5, dtype=torch.float64, device=dev)          # 40 bytes, 8-aligned
+    host_scal = torch.zeros(40, dtype=torch.uint8).pin_memory()
+    hp_dev = {"device_scalars": dev_scal}
+    step = lambda: z.mta_step(gd, replay.begin, replay.plan, hp_dev, rsd_g, W, r, flags=design, ws=ws_g)
+    graph = None
+    if design != z.ONCHIP:
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    for t, lr in [(1, 1e-3), (2, 6e-4), (3, 3e-4), (4, 1e-4)]:
+        hp = hp_at(t, lr=lr)
+        s = z.step_scalars_derive(hp)
+        host_scal.copy_(torch.frombuffer(bytearray(bytes(s)), dtype=torch.uint8))
+        dev_scal.view(torch.uint8).copy_(host_scal, non_blocking=True)
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+        z.mta_step(gd, eager.begin, eager.plan, hp, rsd_e, W, r, flags=design, ws=ws_e)
+        torch.cuda.synchronize()
+        oracle.step([g[eager.begin:eager.begin + eager.S] for g in G], o.master, o.m, o.v, o.param, hp,
+                    part.copy(), r)
+        a, b = eager.gather(), replay.gather()
+        what = f"t={t} design {design}"
+        for k, name in ((0, "master"), (1, "m"), (2, "v")):
+            assert_f32_equal(b[k], a[k], name + " replay vs eager " + what)
+        assert_bf16_equal(b[3], a[3], "param replay vs eager " + what)
+    master, m, v, p = replay.gather()
+    assert_f32_equal(master, o.master, "master vs oracle")
+    assert_f32_equal(m, o.m, "m vs oracle")
+    assert_f32_equal(v, o.v, "v vs oracle")
+    assert_bf16_equal(p, o.param, "param vs oracle")
+    del graph

@@ -42,7 +42,14 @@ class Zero1Error(RuntimeError):
 class HParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("max_norm", ctypes.c_double), ("step", i64)]
+                ("max_norm", ctypes.c_double), ("step", i64), ("device_scalars", P)]
+
+
+class StepScalars(ctypes.Structure):
+    _fields_ = [("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("one_minus_beta1", ctypes.c_float), ("one_minus_beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("step_size", ctypes.c_float), ("decay", ctypes.c_float),
+                ("reserved", ctypes.c_float), ("max_norm", ctypes.c_double)]
 
 
 class NormInfo(ctypes.Structure):
@@ -123,6 +130,8 @@ def lib():
         L.zero1_mta_step.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                      P, i32, i32, u32, P, P, szt, P]
         L.zero1_mta_step.restype = i32
+        L.zero1_step_scalars_derive.argtypes = [ctypes.POINTER(HParams), ctypes.POINTER(StepScalars)]
+        L.zero1_step_scalars_derive.restype = i32
         L.zero1_arena_plan.argtypes = [ctypes.POINTER(ArenaRequest), ctypes.POINTER(ArenaLayout)]
         L.zero1_arena_plan.restype = i32
         _lib = L
@@ -177,10 +186,24 @@ def _ws(ws, ws_bytes):
 
 
 def _hp(hp) -> HParams:
+    """From an HParams, or a dict with lr, beta1, beta2, eps, weight_decay,
+    max_norm, step and optionally device_scalars (a device address or tensor
+    holding a StepScalars; the other keys are then ignored)."""
     if isinstance(hp, HParams):
         return hp
+    dev = hp.get("device_scalars")
+    if dev is not None:
+        return HParams(0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0, _addr(dev))
     return HParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
-                   hp["max_norm"], int(hp["step"]))
+                   hp["max_norm"], int(hp["step"]), None)
+
+
+def step_scalars_derive(hp) -> StepScalars:
+    """The per-step scalars the step calls derive from hp (zero1_step_scalars_derive)."""
+    out = StepScalars()
+    h = _hp(hp)
+    _check(lib().zero1_step_scalars_derive(ctypes.byref(h), ctypes.byref(out)))
+    return out
 
 
 # ------------------------------------------------------------------ ABI

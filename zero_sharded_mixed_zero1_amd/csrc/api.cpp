@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -23,6 +24,10 @@ using namespace z1;
 static_assert(sizeof(NormInfo) == sizeof(zero1_norm_info), "norm info layout");
 static_assert(sizeof(PieceDesc) == 48 && sizeof(ChunkDesc) == 16, "descriptor layout");
 static_assert(kMaxW == ZERO1_MAX_W, "max W");
+static_assert(sizeof(StepScal) == sizeof(zero1_step_scalars) && sizeof(StepScal) == 40 &&
+                  offsetof(StepScal, max_norm) == offsetof(zero1_step_scalars, max_norm) &&
+                  offsetof(StepScal, delta) == offsetof(zero1_step_scalars, decay),
+              "step scalars layout");
 
 namespace {
 
@@ -235,9 +240,21 @@ zero1_status check_flags(uint32_t flags, uint32_t allowed, const char* fn)
     return ZERO1_OK;
 }
 
+zero1_status check_hparam_values(const zero1_hparams* hp);
+
 zero1_status check_hparams(const zero1_hparams* hp)
 {
     if (!hp) return fail(ZERO1_EINVAL, "hp is NULL");
+    if (hp->device_scalars) {   // the values come from device memory; the fields are not read
+        if (reinterpret_cast<uintptr_t>(hp->device_scalars) % 8)
+            return fail(ZERO1_EINVAL, "hp->device_scalars must be 8-byte aligned");
+        return ZERO1_OK;
+    }
+    return check_hparam_values(hp);
+}
+
+zero1_status check_hparam_values(const zero1_hparams* hp)
+{
     if (!(hp->lr >= 0.0) || std::isinf(hp->lr)) return fail(ZERO1_EINVAL, "lr=%g must be finite and >= 0", hp->lr);
     if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(ZERO1_EINVAL, "beta1=%g must be in [0, 1)", hp->beta1);
     if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(ZERO1_EINVAL, "beta2=%g must be in [0, 1)", hp->beta2);
@@ -255,7 +272,12 @@ zero1_status check_hparams(const zero1_hparams* hp)
 Scal scalars(const zero1_hparams* hp, uint32_t flags)
 {
     Scal s;
+    std::memset(&s, 0, sizeof s);
     s.decay_first = (flags & ZERO1_DECAY_FIRST) ? 1 : 0;
+    if (hp->device_scalars) {   // read by the kernels when they run
+        s.dev = static_cast<const StepScal*>(hp->device_scalars);
+        return s;
+    }
     s.b1 = (float)hp->beta1;
     s.b2 = (float)hp->beta2;
     s.a1 = (float)(1.0 - hp->beta1);
@@ -727,6 +749,28 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
     }
     if ((st = zero1_mta_reduce(grads, W, begin, plan, rank_sumsq + my_rank, flags, ws, ws_bytes, stream))) return st;
     return zero1_mta_update(grads, W, begin, plan, hp, rank_sumsq, n_ranks, flags, info_out, ws, ws_bytes, stream);
+}
+
+zero1_status zero1_step_scalars_derive(const zero1_hparams* hp, zero1_step_scalars* out)
+{
+    if (!hp || !out) return fail(ZERO1_EINVAL, "hp or out is NULL");
+    zero1_status st;
+    if ((st = check_hparam_values(hp))) return st;
+    zero1_hparams h = *hp;
+    h.device_scalars = nullptr;
+    const Scal c = scalars(&h, 0);
+    zero1_step_scalars o;
+    std::memset(&o, 0, sizeof o);
+    o.beta1 = c.b1;
+    o.beta2 = c.b2;
+    o.one_minus_beta1 = c.a1;
+    o.one_minus_beta2 = c.a2;
+    o.eps = c.eps;
+    o.step_size = c.sigma;
+    o.decay = c.delta;
+    o.max_norm = hp->max_norm;
+    *out = o;
+    return ok();
 }
 
 zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout* out)

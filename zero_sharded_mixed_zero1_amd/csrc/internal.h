@@ -21,9 +21,16 @@ struct GradPtrs {
 };
 
 // Per-step fp32 scalars, formed in fp64 on the host and rounded once.
+// The device copy of one step's scalars (zero1_step_scalars).
+struct StepScal {
+    float b1, b2, a1, a2, eps, sigma, delta, reserved;
+    double max_norm;
+};
+
 struct Scal {
     float b1, b2, a1, a2, eps, sigma, delta;
-    int decay_first;   // 1: decay the master before the Adam update
+    int decay_first;        // 1: decay the master before the Adam update
+    const StepScal* dev;    // non-null: read b1..delta and max_norm from here at run time
 };
 
 // How the W-slice sum becomes g: keep it, multiply by the exact 2^-k (W a

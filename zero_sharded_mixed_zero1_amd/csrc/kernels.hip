@@ -419,6 +419,18 @@ __device__ __forceinline__ NormInfo clip_info(const double* rank_sumsq, int n_ra
     return norm_info(tot, max_norm, clip_eps);
 }
 
+// Steps replayed from a captured graph carry their per-step scalars in device
+// memory: every update kernel swaps them in before anything else.
+__device__ __forceinline__ void use_device_scalars(Scal& c, double& max_norm)
+{
+    if (c.dev) {
+        const StepScal d = *c.dev;
+        c.b1 = d.b1; c.b2 = d.b2; c.a1 = d.a1; c.a2 = d.a2;
+        c.eps = d.eps; c.sigma = d.sigma; c.delta = d.delta;
+        max_norm = d.max_norm;
+    }
+}
+
 // Prologue of every update kernel: lane 0 forms the clip decision, workgroup 0
 // publishes it, and the whole workgroup reads it from LDS.
 struct ClipArgs {
@@ -550,6 +562,7 @@ template <bool VEC, int GSRC, bool MVBF16>
 __global__ __launch_bounds__(kThreads) void adamw_flat_kernel(Span sp, Reduce r, int64_t len, Scal c,
                                                               ClipArgs ca, int split)
 {
+    use_device_scalars(c, ca.max_norm);
     bool clip;
     float coef;
     block_clip(ca, clip, coef);
@@ -571,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void adamw_mta_kernel(const float* __rest
                                                              const ChunkDesc* __restrict__ chunks,
                                                              int n_chunks, Scal c, ClipArgs ca, int split)
 {
+    use_device_scalars(c, ca.max_norm);
     bool clip;
     float coef;
     block_clip(ca, clip, coef);
@@ -625,6 +639,7 @@ __global__ __launch_bounds__(kThreads, MINW) void onchip_step_kernel(Reduce r, c
                                                                       const ChunkDesc* __restrict__ chunks,
                                                                       int n_chunks, Scal c, OnchipArgs oa)
 {
+    use_device_scalars(c, oa.max_norm);
     float greg[K][8];
     double acc = 0.0;
 #pragma unroll
