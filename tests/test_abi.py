@@ -295,3 +295,21 @@ def test_device_scalars_must_be_aligned():
     hp = z.HParams(0, 0, 0, 0, 0, 0, 0, FAKE + 4)
     assert "aligned" in _einval(lambda: z.adamw_step(FAKE + (4 << 20), None, 0, 100, *bufs, hp,
                                                      FAKE + (5 << 20), 1, stream=0))
+
+
+def test_c_consumer_compiles_and_links(tmp_path):
+    """include/zero1.h is valid C11 and libzero1.so links from C: a small C
+    program calls the host-only entry points (no device work)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    libdir = os.path.dirname(z.lib_path)
+    exe = tmp_path / "abi_consumer"
+    src = os.path.join(ROOT, "tests", "c", "abi_consumer.c")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", str(exe), "-L", libdir, "-lzero1", f"-Wl,-rpath,{libdir}", "-lm"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.strip().endswith("all ok"), out.stdout
