@@ -7,10 +7,11 @@
 //     quads [512w+4l, +4) and [512w+256+4l, +4), so every load or store
 //     instruction of a wave covers one contiguous run (512 B of bf16, 1 KiB of
 //     fp32): fully coalesced for both element sizes.
-//   * Every array is touched once per phase, so all accesses carry the
+//   * Every array but g is touched once per step, so those accesses carry the
 //     non-temporal hint (global_load/store ... nt): streaming data should not
 //     displace anything in L2/MALL.  On MI355X this is worth ~1.5-2x over
-//     plain accesses for these kernels.
+//     plain accesses for these kernels.  g, written by the reduce and read
+//     back by the update, keeps the default policy while it fits the MALL.
 //   * Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs
 //     on XCD b % 8), and each XCD has its own L2 and address-translation
 //     caches.  So the tiles are split into 8 contiguous eighths and XCD x's
