@@ -795,3 +795,36 @@ def test_device_scalars_replay_changes_step_and_lr(env, design):
     assert_f32_equal(v, o.v, "v vs oracle")
     assert_bf16_equal(p, o.param, "param vs oracle")
     del graph
+
+
+def test_workspace_errors(env):
+    """A missing, misaligned or short workspace is rejected (EWORKSPACE) before
+    anything is launched, on every entry point that takes one."""
+    torch, dev = env
+    numels, W, r = RAGGED, 4, 1
+    N = sum(numels)
+    sh = MtaShard(torch, dev, numels, W, r, synth.f32(N, synth.master_key(0xF600), 0, 0.02))
+    G = replicas(0xF600, 1, W, N, 0.02)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    need_mta = z.mta_workspace_bytes(sh.plan, W, z.STORE_G)
+    need_sr = z.workspace_bytes(5000, W)
+    big = torch.empty(need_mta + need_sr + 512, dtype=torch.uint8, device=dev)
+    base = big.data_ptr()
+    calls = {
+        "mta_step": (need_mta, lambda ws, nb: z.mta_step(gd, sh.begin, sh.plan, hp_at(1), rsd, W, r,
+                                                         flags=z.STORE_G, ws=ws, ws_bytes=nb)),
+        "mta_reduce": (need_mta, lambda ws, nb: z.mta_reduce(gd, sh.begin, sh.plan, rsd[r:r + 1],
+                                                             flags=z.STORE_G, ws=ws, ws_bytes=nb)),
+        "shard_reduce": (need_sr, lambda ws, nb: z.shard_reduce(gd, 0, 5000, sumsq_out=rsd[0:1], ws=ws,
+                                                                ws_bytes=nb)),
+    }
+    for name, (need, call) in calls.items():
+        for ws, nb, msg in [(None, None, "NULL"), (base + 16, need, "aligned"), (base, need - 1, "needs")]:
+            with pytest.raises(z.Zero1Error) as e:
+                call(ws, nb)
+            assert e.value.name == "ZERO1_EWORKSPACE", (name, e.value)
+            assert msg in e.value.message, (name, e.value.message)
+    torch.cuda.synchronize()
+    master, m, v, p = sh.gather()
+    assert not m.any() and not v.any(), "a rejected call changed the state"
