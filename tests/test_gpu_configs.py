@@ -266,7 +266,12 @@ def test_dense_7p5b_w64_rank0(env):
     run_large(env, c, 0, c.steps)
 
 
-@pytest.mark.parametrize("rank,steps", [(3, 5), (0, 2)])
+def test_dense_7p5b_w64_last_rank(env):
+    c = configs()["C3"]
+    run_large(env, c, 63, 2)
+
+
+@pytest.mark.parametrize("rank,steps", [(3, 5), (0, 2), (7, 2)])
 def test_llama7b_w8(env, rank, steps):
     c = configs()["C4"]
     run_large(env, c, rank, steps)
