@@ -64,6 +64,180 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# ---------------------------------------------------------------------- setup
+class Copy:
+    """One independent copy of everything a step touches (rotated through so
+    that consecutive steps do not find each other's data in the 256 MB MALL)."""
+
+
+def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
+    """Every array of n_copies independent copies of one rank's step, resident
+    in HBM.  layout "arena": one allocation laid out by zero1_arena_plan (the
+    update's five streams 24 GiB apart, the gradient buffers packed after
+    them); copy c sits c * delta bytes after copy 0, inside copy 0's gaps.
+    layout "packed": one torch allocation per array."""
+    import synth
+    import zero_sharded_mixed_zero1_amd as z
+
+    W, rank = cfg.W, cfg.rank
+    numels = [n for _, n in cfg.tensors]
+    N = sum(numels)
+    begin, S = z.shard_range(N, W, rank)
+    pieces_l = z.shard_pieces(numels, begin, begin + S)
+    offsets = [0]
+    for n in numels:
+        offsets.append(offsets[-1] + n)
+    first, last = pieces_l[0][0], pieces_l[-1][0]
+    p_lo, p_hi = offsets[first], offsets[last + 1]      # the tensors the shard touches
+    grad_elems, grad_off = (N, begin) if cfg.all_replicas_resident else (S, 0)
+    mvdt = torch.int16 if cfg.mv_bf16 else torch.float32
+    mv_flag = z.MV_BF16 if cfg.mv_bf16 else 0
+    arena = None
+    info = {"layout": layout}
+    if layout == "arena":
+        free, _ = torch.cuda.mem_get_info(dev)
+        cap = max(0, free - (8 << 30))
+        L = z.arena_plan(S, W, grad_elems, grad_off, p_hi - p_lo, begin - p_lo,
+                         flags=mv_flag | (design_flags & (z.STORE_G | z.RECOMPUTE_G)), capacity=cap)
+        unit = 2 << 20
+        # copy c is copy 0 shifted by c * delta: delta clears the largest spaced
+        # array and the whole region from the parameter buffer to the end
+        extents = [L.ws_bytes, 4 * S, (2 if cfg.mv_bf16 else 4) * S]
+        delta = (max(extents + [L.total_bytes - L.params]) + unit - 1) // unit * unit
+        total = L.total_bytes + (n_copies - 1) * delta
+        if n_copies > 1 and delta * (n_copies - 1) + max(extents) + 2 * (begin - p_lo) > L.spacing:
+            raise SystemExit("arena: the copies do not fit in the gaps; use --rotate 1 or --layout packed")
+        arena = torch.empty(total, dtype=torch.uint8, device=dev)
+        info.update(arena_bytes=total, spacing_gib=L.spacing / (1 << 30))
+        spans = []
+
+        def view(off, n, dt):
+            nb = n * torch.empty((), dtype=dt).element_size()
+            spans.append((off, off + nb))
+            return arena[off:off + nb].view(dt)
+    copies = []
+    for c in range(n_copies):
+        cp = Copy()
+        if layout == "arena":
+            sh = c * delta
+            bufs = [view(sh + L.grads[w], grad_elems, torch.int16) for w in range(W)]
+            cp.master = view(sh + L.master, S, torch.float32)
+            cp.m = view(sh + L.m, S, mvdt)
+            cp.v = view(sh + L.v, S, mvdt)
+            cp.params = view(sh + L.params, p_hi - p_lo, torch.int16)
+            cp.ws = view(sh + L.ws, L.ws_bytes, torch.uint8)
+        else:
+            bufs = [torch.empty(grad_elems, dtype=torch.int16, device=dev) for _ in range(W)]
+            cp.master = torch.empty(S, dtype=torch.float32, device=dev)
+            cp.m = torch.empty(S, dtype=mvdt, device=dev)
+            cp.v = torch.empty(S, dtype=mvdt, device=dev)
+            cp.params = torch.empty(p_hi - p_lo, dtype=torch.int16, device=dev)
+            cp.ws = None
+        for w, t in enumerate(bufs):
+            synth.fill_bf16_(t, synth.grad_key(cfg.seed, 1, w), begin - grad_off, cfg.sigma, cfg.outlier_pct)
+        if cfg.all_replicas_resident:
+            # every replica's full flat gradient is resident; the step reads rank's slice
+            cp.full = bufs
+            cp.begin = begin
+        else:
+            # only this rank's W slices exist (their global flat indices start at begin)
+            cp.begin = 0
+        cp.grads = bufs
+        synth.fill_f32_(cp.master, synth.master_key(cfg.seed), begin, cfg.master_sigma)
+        cp.m.zero_()
+        cp.v.zero_()
+        cp.params.zero_()
+        # the model's bf16 parameters of the tensors the shard touches (pieces point inside)
+        pieces = [(n, so, cp.params[offsets[ti] - p_lo + off:], cp.master[so:], cp.m[so:], cp.v[so:])
+                  for ti, off, so, n in pieces_l]
+        cp.table = torch.empty(max(256, z.mta_table_bytes(pieces)), dtype=torch.uint8, device=dev)
+        cp.plan = z.mta_plan(pieces, cp.table, flags=mv_flag)
+        if cp.ws is None or cp.ws.numel() < z.mta_workspace_bytes(cp.plan, W, design_flags):
+            cp.ws = torch.empty(z.mta_workspace_bytes(cp.plan, W, design_flags), dtype=torch.uint8, device=dev)
+        cp.rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+        copies.append(cp)
+    if arena is not None:   # no two arrays of any copy overlap (checked before any step runs)
+        spans.sort()
+        for (a0, b0), (a1, b1) in zip(spans, spans[1:]):
+            if b0 > a1:
+                raise SystemExit(f"arena: arrays overlap at byte {a1}")
+    # the other ranks' partial sums of squares (C1/C2: all replicas resident -> true global norm;
+    # otherwise only this rank's slices exist and the other partials are 0: shard-local norm)
+    if cfg.all_replicas_resident:
+        c0 = copies[0]
+        wsr = torch.empty(z.workspace_bytes(S + 8, W), dtype=torch.uint8, device=dev)
+        for r in range(W):
+            b, n = z.shard_range(N, W, r)
+            z.shard_reduce(c0.full, b, n, sumsq_out=c0.rsd[r:r + 1], ws=wsr)
+        torch.cuda.synchronize()
+        for cp in copies[1:]:
+            cp.rsd.copy_(c0.rsd)
+    torch.cuda.synchronize()
+    return dict(W=W, rank=rank, N=N, S=S, begin=begin, pieces=len(pieces_l), copies=copies, info=info)
+
+
+def hp(cfg, t):
+    return cfg.hparams(t)
+
+
+# ---------------------------------------------------------------------- the step
+def run_steps(z, cfg, st, flags, k0, k1, events=None):
+    """Steps k0..k1-1 (t = k+1), rotating through the copies.  With the default
+    design a step is one zero1_mta_step call (a single launch when the shard
+    fits on chip); with an explicit two-phase design it is zero1_mta_reduce +
+    zero1_mta_update.  events[i] = (start, end) brackets the step's dominant
+    kernel: the whole single-launch step, or the update of the two-phase step."""
+    W, rank = st["W"], st["rank"]
+    copies = st["copies"]
+    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
+    for k in range(k0, k1):
+        c = copies[k % len(copies)]
+        h = hp(cfg, k + 1)
+        ev = events[k - k0] if events is not None else None
+        if two_phase:
+            z.mta_reduce(c.grads, c.begin, c.plan, c.rsd[rank:rank + 1], flags=flags, ws=c.ws)
+            if ev:
+                ev[0].record()
+            z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
+        else:
+            if ev:
+                ev[0].record()
+            z.mta_step(c.grads, c.begin, c.plan, h, c.rsd, W, rank, flags=flags, ws=c.ws)
+        if ev:
+            ev[1].record()
+
+
+# ---------------------------------------------------------------------- CPU baseline
+def cpu_baseline(cfg, S_total, begin, budget_s=12.0, max_steps=2000):
+    """The oracle, as it stands, on the same rank's shard (a bounded sample):
+    as many full steps as fit in about budget_s seconds of host time."""
+    import numpy as np
+    import oracle
+    import synth
+
+    W = cfg.W
+    n = min(S_total, 16 * 1024 * 1024)     # at most 16M parameters of the shard
+    grads = [synth.bf16(n, synth.grad_key(cfg.seed, 1, w), begin, cfg.sigma, cfg.outlier_pct) for w in range(W)]
+    master = synth.f32(n, synth.master_key(cfg.seed), begin, cfg.master_sigma)
+    mvd = np.uint16 if cfg.mv_bf16 else np.float32
+    m, v = np.zeros(n, mvd), np.zeros(n, mvd)
+    param = np.zeros(n, np.uint16)
+    rs = np.zeros(W)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step(grads, master, m, v, param, hp(cfg, steps + 1), rs, cfg.rank % W)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= max_steps:
+            break
+    return {"value": n * steps / el, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full oracle steps (reduce, norm, clip, AdamW, bf16) on the first {n:,} "
+                      f"parameters of the same rank's shard, W={W}, {el:.1f} s on {threads} threads"}
+
+
+# ---------------------------------------------------------------------- PMC summary
 def read_pmc_dir(d):
     """{kernel name: [per-dispatch counter values]} from a rocprofv3 --pmc output dir."""
     out = {}

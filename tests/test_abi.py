@@ -313,3 +313,18 @@ def test_c_consumer_compiles_and_links(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0, out.stdout + out.stderr
     assert out.stdout.strip().endswith("all ok"), out.stdout
+
+
+def test_bench_entry_points_and_gpu_count_contract():
+    """bench.py keeps its step machinery, and --gpus N > 1 exits with a message
+    (one GPU is measured) before touching any device."""
+    import subprocess
+    import sys
+    import bench
+    for name in ("setup", "run_steps", "cpu_baseline", "bucketed_timing", "summarize_pmc", "summarize_kt",
+                 "traffic_from_summary", "kernel_source_hash", "main"):
+        assert callable(getattr(bench, name)), name
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 2 and "ONE GPU" in out.stderr, (out.returncode, out.stderr)
+    assert out.stdout == ""
