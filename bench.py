@@ -97,16 +97,24 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
     if layout == "arena":
         free, _ = torch.cuda.mem_get_info(dev)
         cap = max(0, free - (8 << 30))
-        L = z.arena_plan(S, W, grad_elems, grad_off, p_hi - p_lo, begin - p_lo,
-                         flags=mv_flag | (design_flags & (z.STORE_G | z.RECOMPUTE_G)), capacity=cap)
-        unit = 2 << 20
-        # copy c is copy 0 shifted by c * delta: delta clears the largest spaced
-        # array and the whole region from the parameter buffer to the end
-        extents = [L.ws_bytes, 4 * S, (2 if cfg.mv_bf16 else 4) * S]
-        delta = (max(extents + [L.total_bytes - L.params]) + unit - 1) // unit * unit
-        total = L.total_bytes + (n_copies - 1) * delta
-        if n_copies > 1 and delta * (n_copies - 1) + max(extents) + 2 * (begin - p_lo) > L.spacing:
-            raise SystemExit("arena: the copies do not fit in the gaps; use --rotate 1 or --layout packed")
+        try:
+            L = z.arena_plan(S, W, grad_elems, grad_off, p_hi - p_lo, begin - p_lo,
+                             flags=mv_flag | (design_flags & (z.STORE_G | z.RECOMPUTE_G)), capacity=cap)
+        except z.Zero1Error as e:
+            L = None
+            info.update(layout="packed", arena_refused=e.message)
+        if L is not None:
+            unit = 2 << 20
+            # copy c is copy 0 shifted by c * delta: delta clears the largest spaced
+            # array and the whole region from the parameter buffer to the end
+            extents = [L.ws_bytes, 4 * S, (2 if cfg.mv_bf16 else 4) * S]
+            delta = (max(extents + [L.total_bytes - L.params]) + unit - 1) // unit * unit
+            total = L.total_bytes + (n_copies - 1) * delta
+            if n_copies > 1 and delta * (n_copies - 1) + max(extents) + 2 * (begin - p_lo) > L.spacing:
+                L = None
+                info.update(layout="packed", arena_refused="the rotated copies do not fit in the arena's gaps")
+        layout = info["layout"]
+    if layout == "arena":
         arena = torch.empty(total, dtype=torch.uint8, device=dev)
         info.update(arena_bytes=total, spacing_gib=L.spacing / (1 << 30))
         spans = []
