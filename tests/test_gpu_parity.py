@@ -828,3 +828,58 @@ def test_workspace_errors(env):
     torch.cuda.synchronize()
     master, m, v, p = sh.gather()
     assert not m.any() and not v.any(), "a rejected call changed the state"
+
+
+def test_c_program_runs_the_step(env, tmp_path):
+    """tests/c/step_demo.c -- plain C11 over the HIP runtime and libzero1.so,
+    no Python or torch -- runs three steps of a ragged tensor list for one
+    rank; its master, m, v, bf16 params and norm info equal the oracle's."""
+    import shutil
+    import subprocess
+    import os
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(z.lib_path)
+    exe = tmp_path / "step_demo"
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+                    "-isystem", "/opt/rocm/include", "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c", "step_demo.c"), "-o", str(exe), "-L", libdir, "-lzero1",
+                    "-L", "/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"],
+                   check=True)
+    sizes, W, r, steps = RAGGED, 4, 2, 3
+    N = sum(sizes)
+    b, S = z.shard_range(N, W, r)
+    master_full = synth.f32(N, synth.master_key(0xF700), 0, 0.02)
+    Gs = [replicas(0xF700, t, W, N, [0.3, 1e-4, 0.02][t - 1], outlier_pct=1) for t in range(1, steps + 1)]
+    parts = np.array([[oracle.sumsq(oracle.shard_reduce([g[q0:q0 + n] for g in G]))
+                       for q0, n in (z.shard_range(N, W, q) for q in range(W))] for G in Gs])
+    inp, outp = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        f.write(np.array([len(sizes), W, r, steps], dtype=np.int64).tobytes())
+        f.write(np.array(sizes, dtype=np.int64).tobytes())
+        f.write(parts.astype(np.float64).tobytes())
+        f.write(master_full[b:b + S].astype(np.float32).tobytes())
+        for G in Gs:
+            for g in G:
+                f.write(g.astype(np.uint16).tobytes())
+    res = subprocess.run([str(exe), str(inp), str(outp)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    raw = np.fromfile(outp, dtype=np.uint8)
+    master = raw[:4 * S].view(np.float32)
+    m = raw[4 * S:8 * S].view(np.float32)
+    v = raw[8 * S:12 * S].view(np.float32)
+    param = raw[12 * S:14 * S].view(np.uint16)
+    infos = raw[14 * S:].view(np.float64).reshape(steps, 4)
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[b:b + S])
+    for t, G in enumerate(Gs, start=1):
+        oi = oracle.step([g[b:b + S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), parts[t - 1].copy(), r)
+        ni = infos[t - 1]
+        assert rel_close(ni[1], oi.norm, NORM_TOL)
+        assert bool(ni[2:4].view(np.int32)[1]) == oi.clip and ni[2:3].view(np.float32)[0] == oi.coef
+    assert_f32_equal(master, o.master, "master from the C program")
+    assert_f32_equal(m, o.m, "m from the C program")
+    assert_f32_equal(v, o.v, "v from the C program")
+    assert_bf16_equal(param, o.param, "params from the C program")
