@@ -883,3 +883,43 @@ def test_c_program_runs_the_step(env, tmp_path):
     assert_f32_equal(m, o.m, "m from the C program")
     assert_f32_equal(v, o.v, "v from the C program")
     assert_bf16_equal(param, o.param, "params from the C program")
+
+
+def test_two_streams_run_two_ranks_concurrently(env):
+    """Two ranks' steps enqueued on two streams (default priority) at the same
+    time, each with its own workspace: both equal the oracle (the library keeps
+    no per-call state outside the caller's buffers)."""
+    torch, dev = env
+    numels, W, steps = RAGGED, 4, 3
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF800), 0, 0.02)
+    ranks = (0, 3)
+    shards = {r: MtaShard(torch, dev, numels, W, r, master_full) for r in ranks}
+    wss = {r: shards[r].workspace(z.STORE_G) for r in ranks}
+    rsds = {r: torch.zeros(W, dtype=torch.float64, device=dev) for r in ranks}
+    streams = {r: torch.cuda.Stream() for r in ranks}
+    from tests.oracle_sim import RankState
+    ost = {r: RankState(master_full[shards[r].begin:shards[r].begin + shards[r].S]) for r in ranks}
+    for t in range(1, steps + 1):
+        G = replicas(0xF800, t, W, N, [0.3, 0.02, 1e-4][t - 1], outlier_pct=1)
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        part = np.array([oracle.sumsq(oracle.shard_reduce([g[q0:q0 + n] for g in G]))
+                         for q0, n in (z.shard_range(N, W, q) for q in range(W))])
+        for r in ranks:
+            rsds[r].copy_(torch.from_numpy(part))
+        torch.cuda.synchronize()
+        for r in ranks:
+            with torch.cuda.stream(streams[r]):
+                z.mta_step(gd, shards[r].begin, shards[r].plan, hp_at(t), rsds[r], W, r, flags=z.STORE_G,
+                           ws=wss[r], stream=streams[r])
+        torch.cuda.synchronize()
+        for r in ranks:
+            b, S = shards[r].begin, shards[r].S
+            oracle.step([g[b:b + S] for g in G], ost[r].master, ost[r].m, ost[r].v, ost[r].param, hp_at(t),
+                        part.copy(), r)
+    for r in ranks:
+        master, m, v, p = shards[r].gather()
+        assert_f32_equal(master, ost[r].master, f"master rank {r}")
+        assert_f32_equal(m, ost[r].m, f"m rank {r}")
+        assert_f32_equal(v, ost[r].v, f"v rank {r}")
+        assert_bf16_equal(p, ost[r].param, f"param rank {r}")
