@@ -923,3 +923,38 @@ def test_two_streams_run_two_ranks_concurrently(env):
         assert_f32_equal(m, ost[r].m, f"m rank {r}")
         assert_f32_equal(v, ost[r].v, f"v rank {r}")
         assert_bf16_equal(p, ost[r].param, f"param rank {r}")
+
+
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G, z.ONCHIP])
+def test_zero_gradients(env, design):
+    """Degenerate input: every replica's gradient is +0 (step 1) or -0 (step 2),
+    then eps = 0 (step 3, 0/0 by IEEE).  Norm 0, no clip, a pure decay of the
+    master, then NaN everywhere in step 3: all as the oracle."""
+    torch, dev = env
+    numels, W, r = RAGGED8, 4, 1
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF900), 0, 0.02)
+    sh = MtaShard(torch, dev, numels, W, r, master_full)
+    ws = sh.workspace(design)
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[sh.begin:sh.begin + sh.S])
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    info = torch.zeros(4, dtype=torch.float64, device=dev)
+    for t, bits, eps in [(1, 0x0000, 1e-8), (2, 0x8000, 1e-8), (3, 0x0000, 0.0)]:
+        G = [np.full(N, bits, np.uint16) for _ in range(W)]
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        hp = hp_at(t, eps=eps)
+        rsd.zero_()
+        z.mta_step(gd, sh.begin, sh.plan, hp, rsd, W, r, flags=design, info_out=info, ws=ws)
+        torch.cuda.synchronize()
+        oi = oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp, np.zeros(W), r)
+        ni = info.cpu().numpy()
+        assert ni[1] == 0.0 and oi.norm == 0.0
+        assert not ni[2:4].view(np.int32)[1] and ni[2:3].view(np.float32)[0] == np.float32(1.0)
+        master, m, v, p = sh.gather()
+        what = f"t={t} design {design}"
+        assert_f32_equal(master, o.master, "master " + what)
+        assert_f32_equal(m, o.m, "m " + what)
+        assert_f32_equal(v, o.v, "v " + what)
+        assert_bf16_equal(p, o.param, "param " + what)
+    assert np.isnan(master).all()

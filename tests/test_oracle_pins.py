@@ -523,3 +523,33 @@ def test_g_bf16_variant_is_a_step_on_the_rounded_gradient():
     c = [master.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32), np.zeros(N, np.uint16)]
     oracle.step(G, *c, hp_at(1), np.zeros(1), 0)
     assert not np.array_equal(c[0], a[0])
+
+
+def test_zero_gradient_step_is_pure_decay():
+    """Degenerate case: every replica's gradient is zero.  The norm is 0, so
+    nothing is clipped; m and v stay exactly 0 (b*0 + a*0), the Adam term is
+    0/(sqrt(0)+eps) = 0, and the master is only decayed: p*delta, one rounding.
+    With eps = 0 the term is 0/0: NaN by IEEE, which the oracle must carry."""
+    rng = np.random.default_rng(11)
+    N, W = 1000, 3
+    master0 = rng.standard_normal(N).astype(np.float32)
+    zero = [np.zeros(N, np.uint16) for _ in range(W)]
+    for t in (1, 2, 7):
+        master, m, v = master0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+        param = np.zeros(N, np.uint16)
+        rs = np.zeros(1)
+        info = oracle.step(zero, master, m, v, param, hp_at(t), rs, 0)
+        assert info.norm == 0.0 and not info.clip and info.coef == np.float32(1.0)
+        assert not m.any() and not v.any()
+        delta = np.float32(1.0 - 1e-3 * 0.1)
+        assert np.array_equal(master, master0 * delta)
+        assert np.array_equal(param, oracle.f32_to_bf16(master0 * delta))
+    # negative zeros in the gradient behave like +0 (the average of -0 and +0 is +0 or -0; g*g is +0)
+    negz = [np.full(N, 0x8000, np.uint16) for _ in range(W)]
+    master, m, v = master0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+    oracle.step(negz, master, m, v, np.zeros(N, np.uint16), hp_at(1), np.zeros(1), 0)
+    assert np.array_equal(master, master0 * np.float32(1.0 - 1e-3 * 0.1))
+    # eps = 0: 0/0
+    master, m, v = master0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+    oracle.step(zero, master, m, v, np.zeros(N, np.uint16), hp_at(1, eps=0.0), np.zeros(1), 0)
+    assert np.isnan(master).all()
