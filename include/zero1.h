@@ -240,7 +240,7 @@ zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out,
  *   m, v        len fp32 (or bf16 with ZERO1_MV_BF16), updated in place;
  *               zero before the first step.
  *   param_bf16  len bf16 outputs: nearest-even bf16 of the new master.
- *   hp          (host) hyper-parameters; hp->step is t.
+ *   hp          (host) hyper-parameters; hp->step is t (or hp->device_scalars).
  *   rank_sumsq  n_ranks doubles: every rank's partial sum of squares (this
  *               rank's included), added in rank order for the global norm.
  *   flags       ZERO1_MV_BF16; ZERO1_SUM_ONLY and ZERO1_G_BF16 (with g == NULL);
@@ -287,8 +287,10 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads,
  *   with this rank's partial.  Either one cooperative launch (ZERO1_ONCHIP,
  *   on request) or zero1_mta_reduce with sumsq_out = rank_sumsq + my_rank
  *   followed by zero1_mta_update.
- *   flags: one of ZERO1_ONCHIP / ZERO1_STORE_G / ZERO1_RECOMPUTE_G, and
- *   ZERO1_SUM_ONLY (ZERO1_MV_BF16 comes from the plan).
+ *   flags: one of ZERO1_ONCHIP / ZERO1_STORE_G / ZERO1_RECOMPUTE_G (none:
+ *   the library picks, see zero1_mta_design), ZERO1_SUM_ONLY and the
+ *   compatibility variants ZERO1_DECAY_FIRST, ZERO1_CLIP_EPS, ZERO1_G_BF16
+ *   (ZERO1_MV_BF16 comes from the plan).
  * Every design gives bit-identical master, m, v and params for the same
  * clip coefficient; this rank's fp64 partial depends on the launch shape
  * only in its last bits (different fixed summation trees). */
