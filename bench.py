@@ -405,7 +405,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one rank's step on ONE GPU; --gpus {a.gpus} (WORLD_SIZE={world}) is not "
-              "supported: this build has no multi-GPU path (the step shards by construction; see DESIGN.md)",
+              "supported: the library runs one rank's step; several GPUs would each run it on their own shard "
+              "with the exchanges around it, which is not part of this library",
               file=sys.stderr)
         return 2
 
