@@ -70,7 +70,7 @@ class Copy:
     that consecutive steps do not find each other's data in the 256 MB MALL)."""
 
 
-def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
+def setup(torch, cfg, design_flags, n_copies, dev, layout="arena", arena_all=False, arena_offset=0):
     """Every array of n_copies independent copies of one rank's step, resident
     in HBM.  layout "arena": one allocation laid out by zero1_arena_plan (the
     update's five streams 24 GiB apart, the gradient buffers packed after
@@ -115,7 +115,12 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
                 info.update(layout="packed", arena_refused="the rotated copies do not fit in the arena's gaps")
         layout = info["layout"]
     if layout == "arena":
-        arena = torch.empty(total, dtype=torch.uint8, device=dev)
+        base = (int(arena_offset) >> 21) << 21
+        if arena_all:   # the arena takes all free memory (less 8 GB), as a preallocating allocator would
+            if base + total > cap:
+                raise SystemExit("arena: the offset layout does not fit in the free memory")
+            total = max(base + total, cap)
+        arena = torch.empty(total, dtype=torch.uint8, device=dev)[base:]
         info.update(arena_bytes=total, spacing_gib=L.spacing / (1 << 30))
         spans = []
 
@@ -390,6 +395,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="independent copies to rotate (0: auto)")
     ap.add_argument("--layout", choices=["arena", "packed"], default="arena",
                     help="arena: arrays placed by zero1_arena_plan; packed: one torch allocation each")
+    ap.add_argument("--arena-size", choices=["fit", "all"], default="fit",
+                    help="fit: the arena is as large as the plan; all: all free memory less 8 GB")
+    ap.add_argument("--arena-offset-gib", type=float, default=0.0,
+                    help="place the planned layout this far into the arena (tuning; needs --arena-size all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
@@ -421,7 +430,8 @@ def main():
     store_g = bool(flags & z.STORE_G) or (not (flags & (z.RECOMPUTE_G | z.ONCHIP)) and cfg.W > 4)
     per_copy = cfg.S * (2 * cfg.W + 26 + (4 if store_g else 0))
     n_copies = a.rotate or (2 if per_copy < (1 << 30) else 1)
-    st = setup(torch, cfg, flags, n_copies, dev, a.layout)
+    st = setup(torch, cfg, flags, n_copies, dev, a.layout, a.arena_size == "all",
+               int(a.arena_offset_gib * (1 << 30)))
     S, W = st["S"], st["W"]
     c0 = st["copies"][0]
     design = z.mta_design(c0.grads, c0.begin, c0.plan, flags)

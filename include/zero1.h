@@ -352,11 +352,12 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
  * arrays at once depends on how far apart the arrays are: the update's five
  * streams (the reduced gradient g -- or gradient slice 0 when g is recomputed
  * --, master, m, v and the shard's bf16 parameters) run at about 6.2 TB/s when
- * they are 24 GiB or more apart and at about 5.1 TB/s when packed within
- * 12 GiB (Llama-7B/8 shard; 6.7 vs 6.2 TB/s at the GPT-2-small/8 shard).  The
- * planner puts those five at one spacing D (24 GiB, or more when an array is
- * larger, or less when `capacity` is short) and packs the remaining gradient
- * buffers after the parameter buffer.  The gaps between the spaced arrays are
+ * they are far apart and at about 5.1 TB/s when packed within 12 GiB
+ * (Llama-7B/8 shard; 6.7 vs 6.2 TB/s at the GPT-2-small/8 shard), and the
+ * W-slice reduce is faster when the slices sit well away from g (7.5e9/64
+ * shard: 2.40 vs 2.90 ms).  The planner puts those five at one spacing D
+ * (40 GiB, or more when an array is larger, or less when `capacity` is short)
+ * and packs the remaining gradient buffers after the parameter buffer.  The gaps between the spaced arrays are
  * not used by the library: the caller may place its other tensors there.
  *
  * Request: shard_len S >= 1; W in 1..ZERO1_MAX_W gradient buffers of
@@ -396,7 +397,7 @@ typedef struct zero1_arena_layout {
     size_t grads[ZERO1_MAX_W]; /* start of each gradient buffer (element 0) */
 } zero1_arena_layout;
 
-#define ZERO1_ARENA_SPACING ((size_t)24 << 30)   /* preferred spacing D */
+#define ZERO1_ARENA_SPACING ((size_t)40 << 30)   /* preferred spacing D */
 
 zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout* out);
 

@@ -225,7 +225,7 @@ def test_arena_plan_layout(S, W, ge, go, pe, po, flags):
         if cap is None:   # a capacity that forces a smaller spacing
             full = z.arena_plan(S, W, ge, go, pe, po, flags)
             cap = full.total_bytes - 4 * (full.spacing // 3)
-            if full.spacing > 24 * GiB:
+            if full.spacing > 40 * GiB:
                 # the arrays themselves set the spacing: nothing smaller fits
                 assert "packed layout" in _einval(lambda: z.arena_plan(S, W, ge, go, pe, po, flags, capacity=cap))
                 continue
@@ -246,9 +246,9 @@ def test_arena_plan_layout(S, W, ge, go, pe, po, flags):
         assert all(x % UNIT == 0 for x in starts) and L.spacing % UNIT == 0
         assert starts == [base + k * L.spacing for k in range(5)]
         if cap == 1 << 62:
-            assert L.spacing >= 24 * GiB
+            assert L.spacing >= 40 * GiB
         else:
-            assert L.spacing < 24 * GiB
+            assert L.spacing < full.spacing
         # the remaining buffers start on 2 MiB boundaries
         for w in range(0 if store_g else 1, W):
             assert L.grads[w] % UNIT == 0

@@ -813,7 +813,10 @@ zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout
     // the workspace when it is not slot 0
     size_t tail = (size_t)(store_g ? q.W : q.W - 1) * grad_bytes + (store_g ? 0 : round_up(ws_bytes, unit));
     const size_t fixed = base + round_up(slot[4].after, unit) + tail;   // everything but 4 D
-    size_t d = std::max(d_min, ZERO1_ARENA_SPACING);
+    // ZERO1_ARENA_SPACING_MIB overrides the preferred spacing (tuning)
+    static const int spacing_mib = env_int("ZERO1_ARENA_SPACING_MIB", 0);
+    const size_t preferred = spacing_mib > 0 ? round_up((size_t)spacing_mib << 20, unit) : ZERO1_ARENA_SPACING;
+    size_t d = std::max(d_min, preferred);
     if (fixed + 4 * d > q.capacity) {
         if (q.capacity < fixed + 4 * d_min)
             return fail(ZERO1_EINVAL, "capacity %zu bytes is below the packed layout's %zu", q.capacity,
