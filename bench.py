@@ -13,7 +13,7 @@ timed region.  The other ranks' partial sums of squares are computed once
 before timing (they are what a multi-GPU run would exchange mid-step).
 
 Memory: by default every array of the step sits in one allocation laid out by
-zero1_arena_plan (the update's five streams 24 GiB apart; HBM serves them
+zero1_arena_plan (the update's five streams 40 GiB apart; HBM serves them
 faster than arrays packed together); --layout packed allocates each array on
 its own.
 
@@ -73,7 +73,7 @@ class Copy:
 def setup(torch, cfg, design_flags, n_copies, dev, layout="arena", arena_all=False, arena_offset=0):
     """Every array of n_copies independent copies of one rank's step, resident
     in HBM.  layout "arena": one allocation laid out by zero1_arena_plan (the
-    update's five streams 24 GiB apart, the gradient buffers packed after
+    update's five streams 40 GiB apart, the gradient buffers packed after
     them); copy c sits c * delta bytes after copy 0, inside copy 0's gaps.
     layout "packed": one torch allocation per array."""
     import synth
