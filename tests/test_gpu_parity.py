@@ -958,3 +958,37 @@ def test_zero_gradients(env, design):
         assert_f32_equal(v, o.v, "v " + what)
         assert_bf16_equal(p, o.param, "param " + what)
     assert np.isnan(master).all()
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_configurations(env, case):
+    """Seeded random configurations: replica count, tensor list (tiny, medium
+    and large tensors mixed), rank, design, moment storage, state layout,
+    compatibility variant and clip threshold, two steps each, bit-exact
+    against the oracle."""
+    torch, dev = env
+    rng = np.random.default_rng(0xC0FFEE + case)
+    W = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
+    onchip = case % 5 == 4
+    n_t = int(rng.integers(1, 31))
+    kinds = rng.choice(3, size=n_t, p=[0.4, 0.4, 0.2])
+    sizes = [int(rng.integers(1, 41)) if k == 0 else int(rng.integers(100, 5001)) if k == 1
+             else int(rng.integers(10000, 70001)) for k in kinds]
+    if onchip:   # pieces and shard boundaries on 8-element boundaries
+        sizes = [8 * max(1, s // 8) for s in sizes]
+        S0 = -(-sum(sizes) // W)
+        S0 = -(-S0 // 8) * 8
+        sizes[-1] += W * S0 - sum(sizes)
+    design = z.ONCHIP if onchip else int(rng.choice([z.STORE_G, z.RECOMPUTE_G]))
+    mv_bf16 = bool(rng.integers(0, 2))
+    flat_state = bool(rng.integers(0, 2))
+    variant = int(rng.choice([0, 0, oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
+                              oracle.DECAY_FIRST | oracle.CLIP_EPS]))
+    max_norm = float(rng.choice([1.0, 0.05, math.inf]))
+    scale = float(rng.choice([1e-4, 1e-2, 0.3]))
+    r = int(rng.integers(0, W))
+    _, S = z.shard_range(sum(sizes), W, r)
+    if S == 0:
+        r = 0
+    run_mta_all_ranks(torch, dev, sizes, W, 2, 0xE100 + case, design, mv_bf16, flat_state,
+                      lambda t: scale * (1 + t), max_norm=max_norm, ranks=[r], variant=variant)
