@@ -992,3 +992,45 @@ def test_random_configurations(env, case):
         r = 0
     run_mta_all_ranks(torch, dev, sizes, W, 2, 0xE100 + case, design, mv_bf16, flat_state,
                       lambda t: scale * (1 + t), max_norm=max_norm, ranks=[r], variant=variant)
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_bucketed_reduction_random_cuts(env, case):
+    """Buckets cut at random points of the shard (most not on 8-element or
+    tile boundaries, so both the vector and the element paths run), reduced
+    in a random order: the state equals the oracle's step."""
+    torch, dev = env
+    rng = np.random.default_rng(0xB0C4 + case)
+    W = int(rng.choice([2, 4, 8]))
+    numels = RAGGED
+    N = sum(numels)
+    r = int(rng.integers(0, W))
+    master_full = synth.f32(N, synth.master_key(0xE200 + case), 0, 0.02)
+    sh = MtaShard(torch, dev, numels, W, r, master_full)
+    ws = sh.workspace(z.STORE_G)
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[sh.begin:sh.begin + sh.S])
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    for t in (1, 2):
+        cuts = np.unique(np.concatenate([[0, sh.S], rng.integers(1, sh.S, size=int(rng.integers(1, 12)))]))
+        ranges = list(zip(cuts[:-1], cuts[1:]))
+        parts = torch.zeros(len(ranges), dtype=torch.float64, device=dev)
+        G = replicas(0xE200 + case, t, W, N, 0.3, outlier_pct=1)
+        part = np.array([oracle.sumsq(oracle.shard_reduce([g[q0:q0 + n] for g in G]))
+                         for q0, n in (z.shard_range(N, W, q) for q in range(W))])
+        for k in rng.permutation(len(ranges)):
+            lo, hi = (int(x) for x in ranges[k])
+            bucket = [to_dev_u16(torch, g[sh.begin + lo:sh.begin + hi].copy(), dev) for g in G]
+            z.mta_reduce_range(bucket, sh.plan, lo, hi, parts[k:k + 1], flags=z.STORE_G, ws=ws)
+        rsd.copy_(torch.from_numpy(part))
+        z.partials_sum(parts, len(ranges), rsd[r:r + 1])
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        z.mta_update(gd, sh.begin, sh.plan, hp_at(t), rsd, W, flags=z.STORE_G, ws=ws)
+        torch.cuda.synchronize()
+        assert rel_close(rsd[r].item(), part[r], NORM_TOL)
+        oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), part.copy(), r)
+    master, m, v, p = sh.gather()
+    assert_f32_equal(master, o.master, "master")
+    assert_f32_equal(m, o.m, "m")
+    assert_f32_equal(v, o.v, "v")
+    assert_bf16_equal(p, o.param, "param")
