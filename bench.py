@@ -198,8 +198,10 @@ def run_steps(z, cfg, st, flags, k0, k1, events=None):
     """Steps k0..k1-1 (t = k+1), rotating through the copies.  With the default
     design a step is one zero1_mta_step call (a single launch when the shard
     fits on chip); with an explicit two-phase design it is zero1_mta_reduce +
-    zero1_mta_update.  events[i] = (start, end) brackets the step's dominant
-    kernel: the whole single-launch step, or the update of the two-phase step."""
+    zero1_mta_update.  events[i] = (start, end) pairs: for the two-phase step
+    the reduce kernel's and the update kernel's own (zero1_time_next_launch:
+    stamped by each kernel's dispatch, no markers around it); for the single
+    launch, stream markers around the whole call."""
     W, rank = st["W"], st["rank"]
     copies = st["copies"]
     two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
@@ -208,16 +210,18 @@ def run_steps(z, cfg, st, flags, k0, k1, events=None):
         h = hp(cfg, k + 1)
         ev = events[k - k0] if events is not None else None
         if two_phase:
+            if ev:
+                z.time_next_launch(*ev[0])
             z.mta_reduce(c.grads, c.begin, c.plan, c.rsd[rank:rank + 1], flags=flags, ws=c.ws)
             if ev:
-                ev[0].record()
+                z.time_next_launch(*ev[1])
             z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
         else:
             if ev:
-                ev[0].record()
+                ev[0][0].record()
             z.mta_step(c.grads, c.begin, c.plan, h, c.rsd, W, rank, flags=flags, ws=c.ws)
-        if ev:
-            ev[1].record()
+            if ev:
+                ev[0][1].record()
 
 
 # ---------------------------------------------------------------------- CPU baseline
@@ -464,17 +468,25 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gpu_ms_per_step = g0.elapsed_time(g1) / a.steps
-    # the dominant kernel's own duration: the same K steps again, each bracketed
-    # by HIP events on the stream the library launches on (torch's current stream)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    # each kernel's own duration: the same K steps again, the reduce and the
+    # update of each stamped by their own dispatches (HIP events; the single
+    # launch is bracketed by stream markers on the stream it runs on)
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()   # torch creates the event at its first record
+        return e
+
+    events = [((event(), event()), (event(), event())) for _ in range(a.steps)]
+    torch.cuda.synchronize()
     run_steps(z, cfg, st, flags, a.warmup + a.steps, a.warmup + 2 * a.steps, events)
     torch.cuda.synchronize()
-    kern_ms = [e[0].elapsed_time(e[1]) for e in events]
+    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
+    kern_ms = [e[1 if two_phase else 0][0].elapsed_time(e[1 if two_phase else 0][1]) for e in events]
+    red_ms = [e[0][0].elapsed_time(e[0][1]) for e in events] if two_phase else None
     ms_per_step = el * 1e3 / a.steps
     value = S / (ms_per_step * 1e-3)
     bpp = cfg.bytes_per_param
     kern_avg = sum(kern_ms) / len(kern_ms)
-    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
     # algorithmic bytes per launch of the dominant kernel: the whole step
     # (2W+26 B/param) for the single launch; master/m/v read+write and the
     # bf16 write (26 B/param, 18 with bf16 m,v) for the two-phase update
@@ -506,6 +518,7 @@ def main():
         "pct_of_peak_hbm": 100.0 * value * bpp / 1e9 / PEAK_HBM_GBS,
         "gpu_ms_per_step": gpu_ms_per_step,
         "kernel_ms": kern_avg,
+        "reduce_kernel_ms": sum(red_ms) / len(red_ms) if red_ms else None,
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": kern_bytes},

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ZERO1_ABI_VERSION 2
+#define ZERO1_ABI_VERSION 3
 #define ZERO1_MAX_W 128          /* largest number of replicas per call */
 
 typedef enum zero1_status {
@@ -345,6 +345,30 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
                             double* rank_sumsq, int n_ranks, int my_rank,
                             uint32_t flags, zero1_norm_info* info_out,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- timing
+ * Kernel-scoped timing of the step calls, for profiling.  After this call,
+ * the first kernel launched by the calling thread's next call of a step entry
+ * point (zero1_shard_reduce, zero1_grad_norm, zero1_adamw_step,
+ * zero1_mta_reduce, zero1_mta_reduce_range, zero1_partials_sum,
+ * zero1_mta_update, zero1_mta_step) records start_event when its execution
+ * begins and stop_event when it ends; either may be NULL.  The stamps come
+ * from that kernel's own dispatch (hipExtLaunchKernel), with no marker packets
+ * around it, so hipEventElapsedTime(start, stop) is the kernel's duration as a
+ * kernel trace reports it.  Which kernel is first: the reduce of the reduce
+ * calls and of the two-phase zero1_mta_step, the update of zero1_adamw_step
+ * and zero1_mta_update, the sum of squares of zero1_grad_norm, the partials
+ * sum of zero1_partials_sum (and of an empty zero1_shard_reduce /
+ * zero1_grad_norm).  The request is dropped when that call returns, whether
+ * or not it launched anything; a later request replaces an earlier one.
+ *
+ * The events are created and owned by the caller (hipEventCreate, timing
+ * enabled, on the device the step runs on) and must outlive the kernel.
+ * Errors surface in the step call: ZERO1_EHIP when its stream is being
+ * captured into a graph (kernel-scoped events cannot be captured), ZERO1_EINVAL
+ * for the single cooperative launch (ZERO1_ONCHIP), which takes no events.
+ * Host only; always ZERO1_OK. */
+zero1_status zero1_time_next_launch(void* start_event, void* stop_event);
 
 /* ---------------------------------------------------------------- arena
  * Placement of one rank's optimizer arrays inside one device allocation (the

@@ -58,6 +58,8 @@ int main(void)
 
     /* an invalid call is rejected on the host before anything is launched */
     CHECK(zero1_grad_norm(NULL, 10, NULL, NULL, 0, NULL) == ZERO1_EINVAL, "grad norm rejects NULL");
+    /* a timing request with no events is accepted (host only) */
+    CHECK(zero1_time_next_launch(NULL, NULL) == ZERO1_OK, "timing request");
     printf("all ok\n");
     return 0;
 }

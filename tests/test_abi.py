@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = z.lib()
     for n in names:
         assert hasattr(L, n), f"libzero1.so does not export {n}"
-    assert z.abi_version() == 2
+    assert z.abi_version() == 3
 
 
 def test_oracle_and_synth_libraries_load():

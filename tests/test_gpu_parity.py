@@ -1034,3 +1034,89 @@ def test_bucketed_reduction_random_cuts(env, case):
     assert_f32_equal(m, o.m, "m")
     assert_f32_equal(v, o.v, "v")
     assert_bf16_equal(p, o.param, "param")
+
+
+def test_kernel_scoped_timing(env):
+    """zero1_time_next_launch: a timed step gives bit for bit the state of an
+    untimed one; each kernel's own duration is positive and the two together
+    take less than the same calls bracketed by stream markers; a request is
+    dropped when the next step call returns, also when that call fails; a
+    capturing stream and the single cooperative launch refuse it."""
+    torch, dev = env
+    numels, W, r = RAGGED8, 4, 1
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF600), 0, 0.02)
+    timed = MtaShard(torch, dev, numels, W, r, master_full)
+    plain = MtaShard(torch, dev, numels, W, r, master_full)
+    ws_t, ws_p = timed.workspace(z.STORE_G), plain.workspace(z.STORE_G)
+    G = replicas(0xF600, 1, W, N, 0.3, outlier_pct=1)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    part = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                     for b, n in (z.shard_range(N, W, q) for q in range(W))])
+    rsd_t = torch.from_numpy(part.copy()).to(dev)
+    rsd_p = torch.from_numpy(part.copy()).to(dev)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()          # torch creates the event at its first record
+        return e
+
+    for t in (1, 2, 3):
+        hp = hp_at(t)
+        rs, re_, us, ue, m0, m1 = (ev() for _ in range(6))
+        m0.record()
+        z.time_next_launch(rs, re_)
+        z.mta_reduce(gd, timed.begin, timed.plan, rsd_t[r:r + 1], flags=z.STORE_G, ws=ws_t)
+        z.time_next_launch(us, ue)
+        z.mta_update(gd, timed.begin, timed.plan, hp, rsd_t, W, flags=z.STORE_G, ws=ws_t)
+        m1.record()
+        z.mta_step(gd, plain.begin, plain.plan, hp, rsd_p, W, r, flags=z.STORE_G, ws=ws_p)
+        torch.cuda.synchronize()
+        red, upd, whole = rs.elapsed_time(re_), us.elapsed_time(ue), m0.elapsed_time(m1)
+        assert 0 < red and 0 < upd and red + upd < whole, (red, upd, whole)
+        a, b = plain.gather(), timed.gather()
+        for k, name in ((0, "master"), (1, "m"), (2, "v")):
+            assert_f32_equal(b[k], a[k], f"{name} timed vs untimed t={t}")
+        assert_bf16_equal(b[3], a[3], f"param timed vs untimed t={t}")
+        assert rsd_t[r].item() == rsd_p[r].item()
+
+    # dropped when the next step call returns, even a failing one: the later
+    # untimed reduce leaves the two creation stamps as they were
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    before = a.elapsed_time(b)
+    z.time_next_launch(a, b)
+    with pytest.raises(z.Zero1Error) as ei:
+        z.mta_reduce(gd, timed.begin, timed.plan, None, flags=z.STORE_G, ws=ws_t)
+    assert ei.value.name == "ZERO1_EINVAL"
+    z.mta_reduce(gd, timed.begin, timed.plan, rsd_t[r:r + 1], flags=z.STORE_G, ws=ws_t)
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == before
+
+    # the cooperative single launch takes no events
+    z.time_next_launch(a, b)
+    with pytest.raises(z.Zero1Error) as ei:
+        z.mta_step(gd, timed.begin, timed.plan, hp_at(4), rsd_t, W, r, flags=z.ONCHIP,
+                   ws=timed.workspace(z.ONCHIP))
+    assert ei.value.name == "ZERO1_EINVAL" and "timing" in ei.value.message
+
+    # a stream being captured refuses the request before launching; the same
+    # call without it is captured and replays like an eager call
+    q_graph = torch.zeros(1, dtype=torch.float64, device=dev)
+    q_eager = torch.zeros(1, dtype=torch.float64, device=dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    refused = None
+    with torch.cuda.graph(graph):
+        z.time_next_launch(a, b)
+        try:
+            z.mta_reduce(gd, timed.begin, timed.plan, q_graph, flags=z.STORE_G, ws=ws_t)
+        except z.Zero1Error as e:
+            refused = e
+        z.mta_reduce(gd, timed.begin, timed.plan, q_graph, flags=z.STORE_G, ws=ws_t)
+    assert refused is not None and refused.name == "ZERO1_EHIP", refused
+    graph.replay()
+    z.mta_reduce(gd, timed.begin, timed.plan, q_eager, flags=z.STORE_G, ws=ws_p)
+    torch.cuda.synchronize()
+    assert q_graph.item() == q_eager.item() == rsd_p[r].item()
+    del graph

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     abi_version, last_error, shard_range, workspace_bytes,
     shard_reduce, grad_norm, adamw_step,
     mta_table_bytes, mta_plan, mta_workspace_bytes, mta_reduce, mta_update, mta_design, mta_step, mta_reduce_range, partials_sum,
-    arena_plan, step_scalars_derive,
+    arena_plan, step_scalars_derive, time_next_launch,
     lib, lib_path,
 )
 from .layout import shard_pieces  # noqa: F401

@@ -134,6 +134,8 @@ def lib():
         L.zero1_step_scalars_derive.restype = i32
         L.zero1_arena_plan.argtypes = [ctypes.POINTER(ArenaRequest), ctypes.POINTER(ArenaLayout)]
         L.zero1_arena_plan.restype = i32
+        L.zero1_time_next_launch.argtypes = [P, P]
+        L.zero1_time_next_launch.restype = i32
         _lib = L
     return _lib
 
@@ -334,3 +336,23 @@ def arena_plan(shard_len: int, W: int, grad_elems: int, grad_offset: int, param_
     out = ArenaLayout()
     _check(lib().zero1_arena_plan(ctypes.byref(req), ctypes.byref(out)))
     return out
+
+
+def _event(e) -> int:
+    """A hipEvent_t from a raw integer handle or a torch.cuda.Event (torch
+    creates its event at the first record, so an unrecorded one is recorded
+    once on torch's current stream to bring it into existence)."""
+    if e is None:
+        return 0
+    if isinstance(e, int):
+        return e
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
+
+
+def time_next_launch(start=None, stop=None):
+    """The first kernel of this thread's next step call records start/stop
+    (zero1_time_next_launch): start.elapsed_time(stop) is that kernel's own
+    duration.  Events need enable_timing=True."""
+    _check(lib().zero1_time_next_launch(_event(start), _event(stop)))

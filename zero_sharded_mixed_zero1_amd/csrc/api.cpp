@@ -308,6 +308,16 @@ zero1_status check_disjoint(std::vector<Range>& v)
     return ZERO1_OK;
 }
 
+// A timing request (zero1_time_next_launch) lives until the next step entry
+// point returns: that call's first launch takes it, and it is dropped at
+// return whether or not anything was launched.
+struct LaunchRequestScope {
+    LaunchRequestScope() = default;
+    LaunchRequestScope(const LaunchRequestScope&) = delete;
+    LaunchRequestScope& operator=(const LaunchRequestScope&) = delete;
+    ~LaunchRequestScope() { set_launch_events(nullptr, nullptr); }
+};
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -354,6 +364,7 @@ zero1_status zero1_shard_reduce(const uint16_t* const* grads, int W, int64_t beg
                                 uint32_t flags, float* g_out, double* sumsq_out, void* ws,
                                 size_t ws_bytes, void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_shard_reduce")) return fs;
     Reduce r;
     bool vec = false;
@@ -387,6 +398,7 @@ zero1_status zero1_shard_reduce(const uint16_t* const* grads, int W, int64_t beg
 zero1_status zero1_grad_norm(const float* g, int64_t len, double* sumsq_out, void* ws, size_t ws_bytes,
                              void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (len < 0) return fail(ZERO1_EINVAL, "len=%lld is negative", (long long)len);
     if (!sumsq_out) return fail(ZERO1_EINVAL, "sumsq_out is NULL");
     if (!g && len > 0) return fail(ZERO1_EINVAL, "g is NULL");
@@ -413,6 +425,7 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
                               const double* rank_sumsq, int n_ranks, uint32_t flags, zero1_norm_info* info_out,
                               void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_adamw_step")) return fs;
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
@@ -608,6 +621,7 @@ static zero1_status mta_common(const uint16_t* const* grads, int W, int64_t begi
 zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan,
                               double* sumsq_out, uint32_t flags, void* ws, size_t ws_bytes, void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_reduce")) return fs;
     Reduce r;
     bool vec = false, store_g = false;
@@ -629,6 +643,7 @@ zero1_status zero1_mta_reduce_range(const uint16_t* const* grads, int W, const z
                                    int64_t hi, double* sumsq_out, uint32_t flags, void* ws, size_t ws_bytes,
                                    void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_reduce_range")) return fs;
     zero1_status st;
     if (!plan || !plan->table) return fail(ZERO1_EINVAL, "plan is NULL or has no table");
@@ -657,6 +672,7 @@ zero1_status zero1_mta_reduce_range(const uint16_t* const* grads, int W, const z
 
 zero1_status zero1_partials_sum(const double* parts, int n, double* sum_out, void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (n < 0 || n > kMaxPartials) return fail(ZERO1_EINVAL, "n=%d must be in [0, %d]", n, kMaxPartials);
     if ((!parts && n > 0) || !sum_out) return fail(ZERO1_EINVAL, "parts or sum_out is NULL");
     zero1_status st;
@@ -671,6 +687,7 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
                               const zero1_hparams* hp, const double* rank_sumsq, int n_ranks, uint32_t flags,
                               zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_update")) return fs;
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
@@ -718,6 +735,7 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
                             const zero1_hparams* hp, double* rank_sumsq, int n_ranks, int my_rank,
                             uint32_t flags, zero1_norm_info* info_out, void* ws, size_t ws_bytes, void* stream)
 {
+    LaunchRequestScope timing_scope;
     if (zero1_status fs = check_flags(flags, kAllFlags, "zero1_mta_step")) return fs;
     zero1_status st;
     if ((st = check_hparams(hp))) return st;
@@ -725,6 +743,8 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
         return fail(ZERO1_EINVAL, "my_rank=%d must be in [0, n_ranks=%d)", my_rank, n_ranks);
     if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
     if (flags & ZERO1_ONCHIP) {
+        if (launch_events_pending())
+            return fail(ZERO1_EINVAL, "ZERO1_ONCHIP: the cooperative launch does not take timing events");
         Reduce r;
         bool vec = false, store_g = false;
         DevInfo d;
@@ -749,6 +769,12 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
     }
     if ((st = zero1_mta_reduce(grads, W, begin, plan, rank_sumsq + my_rank, flags, ws, ws_bytes, stream))) return st;
     return zero1_mta_update(grads, W, begin, plan, hp, rank_sumsq, n_ranks, flags, info_out, ws, ws_bytes, stream);
+}
+
+zero1_status zero1_time_next_launch(void* start_event, void* stop_event)
+{
+    set_launch_events(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+    return ok();
 }
 
 zero1_status zero1_step_scalars_derive(const zero1_hparams* hp, zero1_step_scalars* out)

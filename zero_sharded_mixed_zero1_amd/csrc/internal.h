@@ -72,7 +72,13 @@ struct ChunkDesc {
     int64_t offset;   // element offset inside the piece
 };
 
-// ---- launchers (kernels.hip); each returns hipGetLastError() after launch.
+// ---- timing request for the next launch on the calling thread
+// (zero1_time_next_launch): the next kernel the launchers below start takes
+// the events (start and stop stamped by its own dispatch) and clears them.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+bool launch_events_pending();
+
+// ---- launchers (kernels.hip); each returns the launch's status.
 // Phase 1: g = reduce(slices) over [0, len); optional fp32 store of g and one
 // fp64 partial sum of squares per workgroup (nblocks of them).
 // `split`: 8 splits the units into one contiguous part per XCD, 1 is a plain

@@ -34,8 +34,11 @@
 // (wave butterfly, then the four waves in order), so a rerun with the same
 // launch shape reproduces every bit, including the norm.
 #include <hip/hip_cooperative_groups.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "internal.h"
 
@@ -716,16 +719,57 @@ __global__ __launch_bounds__(kThreads, MINW) void onchip_step_kernel(Reduce r, c
     }
 }
 
+// ------------------------------------------------------------- launch helper
+// Timing events requested for the next launch on this thread
+// (zero1_time_next_launch): the first kernel launched after the request takes
+// them, stamped by its own dispatch.
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+// Launches kernel<<<grid, kThreads, 0, s>>>(args...), with the arguments
+// converted to the kernel's parameter types; with a timing request pending,
+// through hipExtLaunchKernel so that the events bracket this kernel alone
+// (refused while s is being captured into a graph).
+template <typename... P, typename... A>
+hipError_t run(void (*kernel)(P...), dim3 grid, hipStream_t s, const A&... args)
+{
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> formal{args...};
+    void* argv[sizeof...(P)];
+    std::apply([&argv](auto&... x) {
+        int i = 0;
+        ((argv[i++] = static_cast<void*>(&x)), ...);
+    }, formal);
+    const void* f = reinterpret_cast<const void*>(kernel);
+    if (t_ev_start || t_ev_stop) {
+        const hipEvent_t a = t_ev_start, b = t_ev_stop;
+        t_ev_start = t_ev_stop = nullptr;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        const hipError_t e = hipStreamIsCapturing(s, &cs);
+        if (e != hipSuccess) return e;
+        if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+        return hipExtLaunchKernel(f, grid, dim3(kThreads), argv, 0, s, a, b, 0);
+    }
+    return hipLaunchKernel(f, grid, dim3(kThreads), argv, 0, s);
+}
+
 }  // namespace
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop)
+{
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
+bool launch_events_pending() { return t_ev_start || t_ev_stop; }
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, double* partials,
                          int nblocks, int split, bool g_nt, hipStream_t s)
 {
-    const dim3 grid(nblocks), block(kThreads);
+    const dim3 grid(nblocks);
     const bool store = g_out != nullptr, norm = partials != nullptr;
-#define Z1_REDUCE(V, ST, NO, NT) \
-    hipLaunchKernelGGL((reduce_kernel<V, ST, NO, NT>), grid, block, 0, s, r, len, g_out, partials, split)
+    hipError_t e;
+#define Z1_REDUCE(V, ST, NO, NT) e = run(reduce_kernel<V, ST, NO, NT>, grid, s, r, len, g_out, partials, split)
 #define Z1_REDUCE_V(V)                                                  \
     do {                                                                \
         if (store && norm) {                                            \
@@ -742,23 +786,19 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, d
     else Z1_REDUCE_V(false);
 #undef Z1_REDUCE_V
 #undef Z1_REDUCE
-    return hipGetLastError();
+    return e;
 }
 
 hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials, int nblocks, int split,
                         hipStream_t s)
 {
-    if (vec)
-        hipLaunchKernelGGL((sumsq_kernel<true>), dim3(nblocks), dim3(kThreads), 0, s, g, len, partials, split);
-    else
-        hipLaunchKernelGGL((sumsq_kernel<false>), dim3(nblocks), dim3(kThreads), 0, s, g, len, partials, split);
-    return hipGetLastError();
+    if (vec) return run(sumsq_kernel<true>, dim3(nblocks), s, g, len, partials, split);
+    return run(sumsq_kernel<false>, dim3(nblocks), s, g, len, partials, split);
 }
 
 hipError_t launch_finalize(const double* partials, int nblocks, double* q_out, hipStream_t s)
 {
-    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials, nblocks, q_out);
-    return hipGetLastError();
+    return run(finalize_kernel, dim3(1), s, partials, nblocks, q_out);
 }
 
 hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool vec, bool mv_bf16,
@@ -766,10 +806,11 @@ hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool 
                              const double* rank_sumsq, int n_ranks, double max_norm, int clip_eps,
                              NormInfo* info_out, int nblocks, int split, hipStream_t s)
 {
-    const dim3 grid(nblocks), block(kThreads);
+    const dim3 grid(nblocks);
     const ClipArgs ca{rank_sumsq, n_ranks, max_norm, clip_eps, info_out};
     const Span sp{g, master, m, v, param};
-#define Z1_FLAT(V, GS, MV) hipLaunchKernelGGL((adamw_flat_kernel<V, GS, MV>), grid, block, 0, s, sp, r, len, sc, ca, split)
+    hipError_t e;
+#define Z1_FLAT(V, GS, MV) e = run(adamw_flat_kernel<V, GS, MV>, grid, s, sp, r, len, sc, ca, split)
     const int gs = g ? 0 : 1;
     if (vec) {
         if (gs == 0) { if (mv_bf16) Z1_FLAT(true, 0, true); else Z1_FLAT(true, 0, false); }
@@ -779,7 +820,7 @@ hipError_t launch_adamw_flat(const float* g, const Reduce& r, int64_t len, bool 
         else         { if (mv_bf16) Z1_FLAT(false, 1, true); else Z1_FLAT(false, 1, false); }
     }
 #undef Z1_FLAT
-    return hipGetLastError();
+    return e;
 }
 
 hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks,
@@ -787,9 +828,10 @@ hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pi
                             int n_ranks, double max_norm, int clip_eps, NormInfo* info_out, int nblocks,
                             int split, hipStream_t s)
 {
-    const dim3 grid(nblocks), block(kThreads);
+    const dim3 grid(nblocks);
     const ClipArgs ca{rank_sumsq, n_ranks, max_norm, clip_eps, info_out};
-#define Z1_MTA(V, GS, MV) hipLaunchKernelGGL((adamw_mta_kernel<V, GS, MV>), grid, block, 0, s, g, r, pieces, chunks, n_chunks, sc, ca, split)
+    hipError_t e;
+#define Z1_MTA(V, GS, MV) e = run(adamw_mta_kernel<V, GS, MV>, grid, s, g, r, pieces, chunks, n_chunks, sc, ca, split)
     const int gs = g ? 0 : 1;
     if (vec) {
         if (gs == 0) { if (mv_bf16) Z1_MTA(true, 0, true); else Z1_MTA(true, 0, false); }
@@ -799,7 +841,7 @@ hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pi
         else         { if (mv_bf16) Z1_MTA(false, 1, true); else Z1_MTA(false, 1, false); }
     }
 #undef Z1_MTA
-    return hipGetLastError();
+    return e;
 }
 
 // K tiles held per workgroup and the minimum waves per SIMD the register
