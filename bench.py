@@ -355,9 +355,10 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
     25 MB bucket of the whole model's bf16 gradient is 25e6 / (2 W) of this
     rank's shard elements, rounded to whole 2048-element tiles), buckets in
     reverse order as backward would produce them; what is left after backward
-    is the partials sum and the update.  Returns per step: the GPU time of all
-    bucket reduces (HIP events around each call, summed) and the time from the
-    last bucket to the end of the update (ms)."""
+    is the partials sum and the update.  Returns per step (ms): the GPU time of
+    all bucket calls (stream markers around each call: its reduce and partial
+    kernels, summed), of their reduce kernels alone (kernel-scoped events,
+    summed), and the time from the last bucket to the end of the update."""
     W, rank, S = st["W"], st["rank"], st["S"]
     b = max(2048, bucket_bytes // (2 * W) // 2048 * 2048)
     ranges = [(lo, min(S, lo + b)) for lo in range(0, S, b)][::-1]
@@ -370,13 +371,21 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
         # addresses prepared once, so the timed loop is one C call per bucket
         calls.append([([g.data_ptr() + 2 * (c.begin + lo) for g in c.grads], lo, hi,
                        c.parts.data_ptr() + 8 * (nb - 1 - i)) for i, (lo, hi) in enumerate(ranges)])
-    red_ms, crit_ms = [], []
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()   # torch creates the event at its first record
+        return e
+
+    red_ms, kern_ms, crit_ms = [], [], []
     for k in range(k0, k0 + steps):
         ci = k % len(st["copies"])
         c = st["copies"][ci]
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nb + 1)]
+        ev = [event() for _ in range(2 * nb + 1)]
+        kev = [(event(), event()) for _ in range(nb)]
+        torch.cuda.synchronize()
         for i, (gp, lo, hi, part) in enumerate(calls[ci]):
             ev[2 * i].record()
+            z.time_next_launch(*kev[i])
             z.mta_reduce_range(gp, c.plan, lo, hi, part, flags=z.STORE_G, ws=c.ws, stream=stream)
             ev[2 * i + 1].record()
         z.partials_sum(c.parts, nb, c.rsd[rank:rank + 1], stream=stream)
@@ -384,9 +393,10 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
         ev[2 * nb].record()
         torch.cuda.synchronize()
         red_ms.append(sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(nb)))
+        kern_ms.append(sum(a.elapsed_time(e) for a, e in kev))
         crit_ms.append(ev[2 * nb - 1].elapsed_time(ev[2 * nb]))
     return dict(bucket_params=b, buckets=nb, reduce_ms=sum(red_ms) / steps,
-                after_backward_ms=sum(crit_ms) / steps)
+                reduce_kernels_ms=sum(kern_ms) / steps, after_backward_ms=sum(crit_ms) / steps)
 
 
 def main():
