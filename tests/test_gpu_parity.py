@@ -1120,3 +1120,59 @@ def test_kernel_scoped_timing(env):
     torch.cuda.synchronize()
     assert q_graph.item() == q_eager.item() == rsd_p[r].item()
     del graph
+
+
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
+@pytest.mark.parametrize("fault", ["nan_partial", "bit_flip", "inf_grad"])
+def test_failure_injection(env, design, fault):
+    """Faults forced from the host; the GPU step and the oracle agree on each:
+    another rank's partial missing (NaN in its rank_sumsq entry) gives a NaN
+    norm, no clip and the nonfinite flag; a flipped exponent bit in one
+    replica's slice gives the same (wrong) step on both sides, which nothing
+    in the step can detect; +inf in one gradient gives an infinite norm, a
+    coefficient of 0 and NaN at that element only."""
+    torch, dev = env
+    from tests.oracle_sim import RankState
+    numels, W, r = RAGGED8, 4, 1
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF700), 0, 0.02)
+    sh = MtaShard(torch, dev, numels, W, r, master_full)
+    ws = sh.workspace(design)
+    o = RankState(master_full[sh.begin:sh.begin + sh.S])
+    G = replicas(0xF700, 1, W, N, 0.3, outlier_pct=1)
+    k = sh.begin + 1234                      # an element of this rank's shard
+    if fault == "bit_flip":
+        G[2][k] ^= 0x4000                    # the exponent's top bit
+    elif fault == "inf_grad":
+        G[0][k] = 0x7F80                     # +inf
+    part = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                     for b, n in (z.shard_range(N, W, q) for q in range(W))])
+    if fault == "nan_partial":
+        part[3] = np.nan                     # rank 3's partial never arrived
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    rsd = torch.from_numpy(part.copy()).to(dev)
+    info = torch.zeros(4, dtype=torch.float64, device=dev)
+    z.mta_step(gd, sh.begin, sh.plan, hp_at(1), rsd, W, r, flags=design, info_out=info, ws=ws)
+    orank = part.copy()
+    oi = oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp_at(1), orank, r)
+    torch.cuda.synchronize()
+    what = f"{fault} design {design}"
+    master, m, v, p = sh.gather()
+    assert_f32_equal(master, o.master, "master " + what)
+    assert_f32_equal(m, o.m, "m " + what)
+    assert_f32_equal(v, o.v, "v " + what)
+    assert_bf16_equal(p, o.param, "param " + what)
+    assert sh.untouched_outside()
+    ni = info.cpu().numpy()
+    iw = ni.view(np.int32)
+    assert rel_close(ni[1], oi.norm, NORM_TOL) and rel_close(rsd[r].item(), orank[r], NORM_TOL)
+    assert bool(iw[5]) == oi.clip and ni[2:3].view(np.float32)[0] == np.float32(oi.coef)
+    assert iw[6] == int(not math.isfinite(oi.norm))
+    if fault == "inf_grad":
+        assert math.isinf(oi.norm) and oi.clip and oi.coef == 0.0
+        j = k - sh.begin
+        assert np.isnan(master[j]) and np.isnan(o.master).sum() == 1
+    elif fault == "nan_partial":
+        assert math.isnan(oi.norm) and not oi.clip
+    else:
+        assert math.isfinite(oi.norm) and oi.norm > 1e30 and oi.clip   # 0.3-ish value -> ~1e38
