@@ -1176,3 +1176,82 @@ def test_failure_injection(env, design, fault):
         assert math.isnan(oi.norm) and not oi.clip
     else:
         assert math.isfinite(oi.norm) and oi.norm > 1e30 and oi.clip   # 0.3-ish value -> ~1e38
+
+
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
+def test_zero1_equals_ddp_on_gpu(env, design):
+    """ZeRO-1 is DDP with the optimizer state sharded: W ranks each reducing
+    their slice, exchanging one partial each and updating their shard give,
+    concatenated, bit for bit the state of one non-sharded step on the whole
+    averaged gradient (norm from a single partial), over three steps."""
+    torch, dev = env
+    numels, W = RAGGED8, 4
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xF800), 0, 0.02)
+    ranks = [MtaShard(torch, dev, numels, W, q, master_full) for q in range(W)]
+    whole = MtaShard(torch, dev, numels, 1, 0, master_full)
+    ws = [sh.workspace(design) for sh in ranks]
+    ws_whole = whole.workspace(design)
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    q_whole = torch.zeros(1, dtype=torch.float64, device=dev)
+    info_r = torch.zeros(4, dtype=torch.float64, device=dev)
+    info_w = torch.zeros(4, dtype=torch.float64, device=dev)
+    for t in (1, 2, 3):
+        G = replicas(0xF800, t, W, N, 0.3 if t != 2 else 0.001, outlier_pct=1)   # clip, no clip, clip
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        hp = hp_at(t)
+        for q, sh in enumerate(ranks):       # every rank's reduce, then the exchange of partials
+            z.mta_reduce(gd, sh.begin, sh.plan, rsd[q:q + 1], flags=design, ws=ws[q])
+        for q, sh in enumerate(ranks):
+            z.mta_update(gd, sh.begin, sh.plan, hp, rsd, W, flags=design, info_out=info_r, ws=ws[q])
+        z.mta_step(gd, 0, whole.plan, hp, q_whole, 1, 0, flags=design, info_out=info_w, ws=ws_whole)
+        torch.cuda.synchronize()
+        ni_r, ni_w = info_r.cpu().numpy(), info_w.cpu().numpy()
+        assert rel_close(ni_r[1], ni_w[1], NORM_TOL)
+        assert ni_r[2:3].view(np.float32)[0] == ni_w[2:3].view(np.float32)[0], "clip coefficients differ"
+        parts = [sh.gather() for sh in ranks]
+        ref = whole.gather()
+        what = f"t={t} design {design}"
+        for k, name in ((0, "master"), (1, "m"), (2, "v")):
+            assert_f32_equal(np.concatenate([p[k] for p in parts]), ref[k], f"{name} ZeRO-1 vs DDP {what}")
+        assert_bf16_equal(np.concatenate([p[3] for p in parts]), ref[3], f"param ZeRO-1 vs DDP {what}")
+
+
+def test_clip_threshold_is_strict(env):
+    """Gradients of ±0.5 make every square and every partial sum exact, so the
+    norm is exactly 256 on both sides whatever the summation order: a norm
+    equal to max_norm is not clipped, one ulp of max_norm below it is (with
+    the coefficient rounding to 1.0f), and max_norm = 128 halves g; the state
+    matches the oracle each time."""
+    torch, dev = env
+    W, N = 2, 262144                        # 262144 * 0.25 = 65536 = 256^2
+    sign = np.where(synth.bf16(N, synth.grad_key(0xF900, 1, 0), 0, 1.0) & 0x8000, 0xBF00, 0x3F00).astype(np.uint16)
+    G = [sign.copy(), sign.copy()]          # both replicas ±0.5: g = ±0.5
+    master0 = synth.f32(N, synth.master_key(0xF900), 0, 0.02)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    ws = ws_tensor(torch, z.workspace_bytes(N, W, z.STORE_G), dev)
+    g = torch.empty(N, dtype=torch.float32, device=dev)
+    for max_norm, clip, coef in [(256.0, False, 1.0), (math.nextafter(256.0, 0.0), True, 1.0),
+                                 (128.0, True, 0.5), (math.nextafter(256.0, math.inf), False, 1.0)]:
+        q = torch.zeros(1, dtype=torch.float64, device=dev)
+        z.shard_reduce(gd, 0, N, g_out=g, sumsq_out=q, ws=ws)
+        gm = torch.from_numpy(master0.copy()).to(dev)
+        gmm = torch.zeros(N, dtype=torch.float32, device=dev)
+        gvv = torch.zeros(N, dtype=torch.float32, device=dev)
+        gp = torch.zeros(N, dtype=torch.int16, device=dev)
+        info = torch.zeros(4, dtype=torch.float64, device=dev)
+        hp = hp_at(1, max_norm=max_norm)
+        z.adamw_step(g, None, 0, N, gm, gmm, gvv, gp, hp, q, 1, info_out=info)
+        om, ov = np.zeros(N, np.float32), np.zeros(N, np.float32)
+        omaster, oparam = master0.copy(), np.zeros(N, np.uint16)
+        oi = oracle.step(G, omaster, om, ov, oparam, hp, np.zeros(1), 0)
+        torch.cuda.synchronize()
+        ni = info.cpu().numpy()
+        assert q.item() == 65536.0 and ni[1] == 256.0 and oi.norm == 256.0
+        assert bool(ni.view(np.int32)[5]) == clip == oi.clip, max_norm
+        assert ni[2:3].view(np.float32)[0] == np.float32(coef) == np.float32(oi.coef), max_norm
+        what = f"max_norm={max_norm!r}"
+        assert_f32_equal(gm.cpu().numpy(), omaster, "master " + what)
+        assert_f32_equal(gmm.cpu().numpy(), om, "m " + what)
+        assert_f32_equal(gvv.cpu().numpy(), ov, "v " + what)
+        assert_bf16_equal(to_np_u16(gp), oparam, "param " + what)
