@@ -249,9 +249,16 @@ def cpu_baseline(cfg, S_total, begin, budget_s=12.0, max_steps=2000):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= max_steps:
             break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": n * steps / el, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} full oracle steps (reduce, norm, clip, AdamW, bf16) on the first {n:,} "
-                      f"parameters of the same rank's shard, W={W}, {el:.1f} s on {threads} threads"}
+                      f"parameters of the same rank's shard, W={W}, {el:.1f} s on {threads} threads",
+            "cpu": cpu, "host_cpus": os.cpu_count()}
 
 
 # ---------------------------------------------------------------------- PMC summary
