@@ -46,7 +46,7 @@ UPDATE_KERNEL = "adamw_mta_kernel"
 ONCHIP_KERNEL = "onchip_step_kernel"
 REDUCE_KERNEL = "reduce_kernel"
 CALIB_BYTES = 1 << 30          # the plain copy used to scale the PMC byte counters
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "zero1_step_gpt2small_w8_pmc.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_mta_kernel_gpt2small_w8_pmc.txt")
 
 
 def kernel_source_hash() -> str:
