@@ -538,6 +538,21 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": kern_bytes},
     }
+    if red_ms:
+        # both kernels of the two-phase step: bytes the step's algorithm needs
+        # and bytes the design moves (+ the fp32 g written and re-read, or the
+        # slices re-read), over each kernel's own time
+        red_avg = sum(red_ms) / len(red_ms)
+        store_g = bool(flags & z.STORE_G)
+        red_alg, red_mv = 2 * W * S, (2 * W + (4 if store_g else 0)) * S
+        upd_mv = kern_bytes + (4 if store_g else 2 * W) * S
+        out["kernels"] = {
+            "reduce": {"ms": red_avg, "algorithmic_bytes": red_alg, "moved_bytes": red_mv,
+                       "algorithmic_GBps": red_alg / (red_avg * 1e-3) / 1e9,
+                       "moved_GBps": red_mv / (red_avg * 1e-3) / 1e9},
+            "update": {"ms": kern_avg, "algorithmic_bytes": kern_bytes, "moved_bytes": upd_mv,
+                       "algorithmic_GBps": achieved, "moved_GBps": upd_mv / (kern_avg * 1e-3) / 1e9},
+        }
     if flags & z.STORE_G:
         out["bucketed"] = bucketed_timing(torch, z, cfg, st, a.warmup + 2 * a.steps, min(a.steps, 50))
     if not a.no_cpu_baseline:
