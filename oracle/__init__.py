@@ -20,7 +20,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "zero1_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB loads another build of the same source (the mutation test points
+# it at builds with planted mistakes, to show that the pins catch them)
+_BUILT = os.path.join(_HERE, "liboracle.so")
+_LIB_PATH = os.environ.get("ORACLE_LIB") or _BUILT
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
              "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -30,10 +33,10 @@ NORM_BLOCK = 65536
 
 def build() -> str:
     """Compile liboracle.so with gcc (always recompiles)."""
-    tmp = _LIB_PATH + ".tmp"
+    tmp = _BUILT + ".tmp"
     subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, _BUILT)
+    return _BUILT
 
 
 _lib = None

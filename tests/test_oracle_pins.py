@@ -190,6 +190,32 @@ def test_update_then_decay_order():
     assert np.any(diff != 0)
 
 
+def test_bf16_moments_are_the_fp32_step_rounded():
+    """Reading 9 (bf16 m, v): each step widens the stored moments, runs the
+    fp32 step, stores the nearest-even bf16 of the new moments and updates the
+    master with the unrounded fp32 ones.  Checked against the fp32-moment path
+    started from the same widened moments, with torch's bfloat16 conversion
+    (a library routine) as the rounding reference."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(9)
+    n = 20000
+    master = rng.standard_normal(n).astype(np.float32) * np.float32(0.02)
+    mb, vb = np.zeros(n, np.uint16), np.zeros(n, np.uint16)
+    pb = np.zeros(n, np.uint16)
+    for t in (1, 2, 3):
+        g = (rng.standard_normal(n) * 0.05).astype(np.float32)
+        s = oracle.adamw_scalars(1e-3, 0.9, 0.95, 1e-8, 0.1, t)
+        pa, ma, va = master.copy(), oracle.bf16_to_f32(mb).copy(), oracle.bf16_to_f32(vb).copy()
+        param_a = np.zeros(n, np.uint16)
+        oracle.adamw(g, pa, ma, va, param_a, s, False, 1.0)
+        oracle.adamw(g, master, mb, vb, pb, s, False, 1.0)
+        rne = lambda x: torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(mb, rne(ma)) and np.array_equal(vb, rne(va)), f"t={t}"
+        assert np.array_equal(master.view(np.uint32), pa.view(np.uint32)), f"t={t}"
+        assert np.array_equal(pb, param_a) and np.array_equal(pb, rne(master)), f"t={t}"
+        assert np.any(oracle.bf16_to_f32(mb) != ma)   # the rounding is visible
+
+
 def test_scalars():
     for t in (1, 2, 10, 1000):
         s = oracle.adamw_scalars(1e-3, 0.9, 0.95, 1e-8, 0.1, t)
