@@ -508,6 +508,37 @@ def test_decay_first_closed_form_and_gap():
     assert 0 < gap <= bound + 1e-6
 
 
+def test_decay_order_gap_has_the_pages_order_of_magnitude():
+    """The page runs its AdamW (update, then decay) against torch's (decay,
+    then update) for 100 steps on a quadratic and reports a largest difference
+    of 8.4e-4, which it attributes to the order alone (a term of order
+    lr^2*lambda per step).  The page gives neither the quadratic nor the
+    hyper-parameters, so the exact figure stays unpinned; under the reading
+    f(x) = x^2/2 from x = 1, lr = 1e-2, lambda = 0.1, betas (0.9, 0.999),
+    eps = 1e-8 the two orders end up differing by the same order of magnitude
+    (about 4.6e-4), and the gap grows with lr^2*lambda as the page says."""
+    def run(lr, wd, variant):
+        x = np.array([1.0], np.float32)
+        m = np.zeros(1, np.float32)
+        v = np.zeros(1, np.float32)
+        out = []
+        for t in range(1, 101):
+            hp = dict(lr=lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd, max_norm=math.inf, step=t)
+            oracle.step([oracle.f32_to_bf16(x.copy())], x, m, v, oracle.f32_to_bf16(x), hp, np.zeros(1), 0,
+                        variant=variant)
+            out.append(float(x[0]))
+        return np.array(out)
+
+    def gap(lr, wd):
+        return float(np.max(np.abs(run(lr, wd, 0) - run(lr, wd, oracle.DECAY_FIRST))))
+
+    g = gap(1e-2, 0.1)
+    assert 1e-4 < g < 1e-2 and abs(math.log10(g) - math.log10(8.4e-4)) < 0.5, g
+    # scaling: ten times lambda, or about ten times lr^2, gives a gap ten times larger or so
+    assert 5 < gap(1e-2, 0.1) / gap(1e-2, 0.01) < 20
+    assert 3 < gap(1e-2, 0.1) / gap(3e-3, 0.1) < 30
+
+
 def test_torch_clip_convention_against_torch():
     """The torch clip variant reproduces torch.nn.utils.clip_grad_norm_'s
     coefficient (max_norm / (norm + 1e-6), clamped at 1; fp64 gradients)."""
