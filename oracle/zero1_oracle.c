@@ -24,8 +24,9 @@
  *
  * Parity pins: each function is pinned by tests under tests/ (worked examples,
  * closed forms, exact-rational re-evaluation, library RNE).  Nothing here is
- * "parity unpinned" except the 100-step AdamW-vs-torch figure on [PT], which
- * the oracle does not attempt to reproduce.
+ * "parity unpinned" except the exact 100-step AdamW-vs-torch figure on [PT]
+ * (the page gives neither its quadratic nor its hyper-parameters; only the
+ * order of magnitude is pinned, under a stated reading of both).
  */
 #include <math.h>
 #include <stdint.h>
