@@ -1255,3 +1255,71 @@ def test_clip_threshold_is_strict(env):
         assert_f32_equal(gmm.cpu().numpy(), om, "m " + what)
         assert_f32_equal(gvv.cpu().numpy(), ov, "v " + what)
         assert_bf16_equal(to_np_u16(gp), oparam, "param " + what)
+
+
+def test_host_threads_step_ranks_concurrently(env):
+    """Four host threads, one rank each, step their ranks at the same time on
+    their own streams (the binding releases the interpreter lock during each
+    call), interleaved with rejected calls whose messages each thread reads
+    back: every rank equals the oracle, and every thread sees its own error
+    message (the library's error state is per thread)."""
+    import threading
+    torch, dev = env
+    from tests.oracle_sim import RankState
+    numels, W, steps = RAGGED8, 4, 3
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0xFA00), 0, 0.02)
+    ranks = (0, 1, 2, 3)
+    shards = {r: MtaShard(torch, dev, numels, W, r, master_full) for r in ranks}
+    wss = {r: shards[r].workspace(z.STORE_G) for r in ranks}
+    rsds = {r: torch.zeros(W, dtype=torch.float64, device=dev) for r in ranks}
+    Gs, gds, parts = [], [], []
+    for t in range(1, steps + 1):
+        G = replicas(0xFA00, t, W, N, [0.3, 0.02, 1e-4][t - 1], outlier_pct=1)
+        Gs.append(G)
+        gds.append([to_dev_u16(torch, g, dev) for g in G])
+        parts.append(np.array([oracle.sumsq(oracle.shard_reduce([g[q0:q0 + n] for g in G]))
+                               for q0, n in (z.shard_range(N, W, q) for q in range(W))]))
+    torch.cuda.synchronize()
+    barrier = threading.Barrier(len(ranks))
+    failures = []
+
+    def worker(r):
+        try:
+            torch.cuda.set_device(dev)
+            s = torch.cuda.Stream()
+            for t in range(1, steps + 1):
+                rsds[r].copy_(torch.from_numpy(parts[t - 1]))
+                torch.cuda.synchronize()
+                barrier.wait()
+                z.mta_step(gds[t - 1], shards[r].begin, shards[r].plan, hp_at(t), rsds[r], W, r, flags=z.STORE_G,
+                           ws=wss[r], stream=s)
+                try:
+                    z.shard_range(10, 0, r)          # rejected: W = 0
+                except z.Zero1Error as e:
+                    if "W=0" not in e.message:
+                        failures.append(f"rank {r}: foreign error message {e.message!r}")
+                else:
+                    failures.append(f"rank {r}: W = 0 accepted")
+                s.synchronize()
+        except Exception as e:  # noqa: BLE001 - reported below
+            failures.append(f"rank {r}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(r,)) for r in ranks]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    assert not failures, failures
+    for r in ranks:
+        o = RankState(master_full[shards[r].begin:shards[r].begin + shards[r].S])
+        b, S = shards[r].begin, shards[r].S
+        for t in range(1, steps + 1):
+            oracle.step([g[b:b + S] for g in Gs[t - 1]], o.master, o.m, o.v, o.param, hp_at(t),
+                        parts[t - 1].copy(), r)
+        master, m, v, p = shards[r].gather()
+        assert_f32_equal(master, o.master, f"master rank {r}")
+        assert_f32_equal(m, o.m, f"m rank {r}")
+        assert_f32_equal(v, o.v, f"v rank {r}")
+        assert_bf16_equal(p, o.param, f"param rank {r}")
