@@ -209,7 +209,7 @@ def lib_flags(variant):
 
 
 def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_state, sigma_fn,
-                      max_norm=1.0, ranks=None, variant=0):
+                      max_norm=1.0, ranks=None, variant=0, sum_only=False):
     N = sum(numels)
     ranks = list(range(W)) if ranks is None else ranks
     master_full = synth.f32(N, synth.master_key(seed), 0, 0.02)
@@ -226,12 +226,13 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
         part = np.zeros(W)
         for r in range(W):
             b, e = shard_range(N, W, r)
-            gr = oracle.shard_reduce([g[b:e] for g in G])
+            gr = oracle.shard_reduce([g[b:e] for g in G], average=not sum_only)
             if variant & oracle.G_BF16:
                 gr = oracle.round_to_bf16(gr)
             part[r] = oracle.sumsq(gr)
             # every rank's partial from the GPU (what the mid-step exchange would deliver)
-            z.shard_reduce(gd, b, e - b, sumsq_out=rsd[r:r + 1], flags=lib_flags(variant), ws=ws_r)
+            z.shard_reduce(gd, b, e - b, sumsq_out=rsd[r:r + 1], flags=lib_flags(variant) | (z.SUM_ONLY if sum_only else 0),
+                           ws=ws_r)
         torch.cuda.synchronize()
         gpu_part = rsd.cpu().numpy().copy()
         for r in range(W):
@@ -241,10 +242,10 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
             b, e = shard_range(N, W, r)
             rs = part.copy()
             oi = oracle.step([g[b:e] for g in G], ost[r].master, ost[r].m, ost[r].v, ost[r].param, hp, rs, r,
-                             variant=variant)
+                             average=not sum_only, variant=variant)
             rsd.copy_(torch.from_numpy(gpu_part))
-            z.mta_step(gd, b, shards[r].plan, hp, rsd, W, r, flags=flags | lib_flags(variant), info_out=infos[r],
-                       ws=wss[r])
+            z.mta_step(gd, b, shards[r].plan, hp, rsd, W, r,
+                       flags=flags | lib_flags(variant) | (z.SUM_ONLY if sum_only else 0), info_out=infos[r], ws=wss[r])
             torch.cuda.synchronize()
             ni = infos[r].cpu().numpy()
             assert rel_close(ni[1], oi.norm, NORM_TOL)
@@ -280,6 +281,17 @@ def test_mta_parity_state_layouts(env, mv_bf16, flat_state):
     for design in (z.ONCHIP, z.STORE_G, z.RECOMPUTE_G):
         run_mta_all_ranks(torch, dev, ragged_for(design), 4, 3, 0xB000, design, mv_bf16, flat_state,
                           lambda t: [0.02, 1e-4, 0.3][t % 3])
+
+
+@pytest.mark.parametrize("W", [3, 8])
+@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+def test_mta_sum_only_parity(env, W, design):
+    """ZERO1_SUM_ONLY (the reduce keeps the sum, no average) through the whole
+    multi-tensor step on every design, every rank, against the oracle's
+    unaveraged step."""
+    torch, dev = env
+    run_mta_all_ranks(torch, dev, ragged_for(design), W, 2, 0xD800 + W, design, False, True,
+                      lambda t: 0.05, sum_only=True)
 
 
 @pytest.mark.parametrize("variant", [oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
