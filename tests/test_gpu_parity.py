@@ -209,7 +209,7 @@ def lib_flags(variant):
 
 
 def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_state, sigma_fn,
-                      max_norm=1.0, ranks=None, variant=0, sum_only=False):
+                      max_norm=1.0, ranks=None, variant=0, sum_only=False, hp_kw=None):
     N = sum(numels)
     ranks = list(range(W)) if ranks is None else ranks
     master_full = synth.f32(N, synth.master_key(seed), 0, 0.02)
@@ -237,7 +237,7 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
         gpu_part = rsd.cpu().numpy().copy()
         for r in range(W):
             assert rel_close(gpu_part[r], part[r], NORM_TOL)
-        hp = hp_at(t, max_norm=max_norm)
+        hp = hp_at(t, max_norm=max_norm, **(hp_kw or {}))
         for r in ranks:
             b, e = shard_range(N, W, r)
             rs = part.copy()
@@ -292,6 +292,36 @@ def test_mta_sum_only_parity(env, W, design):
     torch, dev = env
     run_mta_all_ranks(torch, dev, ragged_for(design), W, 2, 0xD800 + W, design, False, True,
                       lambda t: 0.05, sum_only=True)
+
+
+# Edge values of the hyper-parameters the boundary accepts: no moment memory
+# (beta 0: m = g, v = g*g), no step (lr 0: sigma 0, decay factor 1), no decay,
+# moments that forget almost nothing (bias corrections near 1e-6 at t = 1, so
+# sigma is lr * 1e3), an eps that dominates sqrt(v), a large step, and a decay
+# factor 1 - lr*wd that is negative.
+DEGENERATE_HP = {
+    "beta1=0": dict(beta1=0.0),
+    "beta2=0": dict(beta2=0.0),
+    "beta1=beta2=0": dict(beta1=0.0, beta2=0.0),
+    "lr=0": dict(lr=0.0),
+    "wd=0": dict(weight_decay=0.0),
+    "beta=1-1e-6": dict(beta1=1.0 - 1e-6, beta2=1.0 - 1e-6),
+    "eps=1": dict(eps=1.0),
+    "lr=10": dict(lr=10.0, weight_decay=0.05),
+    "decay factor -1": dict(lr=1.0, weight_decay=2.0),
+}
+
+
+@pytest.mark.parametrize("name", list(DEGENERATE_HP))
+@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+def test_degenerate_hyperparameters(env, name, design):
+    """Every design on a ragged list, three steps, one rank (fp32 moments) and
+    another (bf16 moments), bit-exact against the oracle."""
+    torch, dev = env
+    kw = DEGENERATE_HP[name]
+    for r, mv_bf16 in ((1, False), (2, True)):
+        run_mta_all_ranks(torch, dev, ragged_for(design), 3, 3, 0xDE00 + r, design, mv_bf16, True,
+                          lambda t: [0.02, 1e-4, 0.3][t % 3], ranks=[r], hp_kw=kw)
 
 
 @pytest.mark.parametrize("variant", [oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
