@@ -539,6 +539,52 @@ def test_decay_order_gap_has_the_pages_order_of_magnitude():
     assert 3 < gap(1e-2, 0.1) / gap(3e-3, 0.1) < 30
 
 
+@pytest.mark.parametrize("order", ["update_then_decay", "decay_first"])
+@pytest.mark.parametrize("lr,b2,eps", [(1e-2, 0.99, 1e-6), (1e-3, 0.95, 1e-8)])
+def test_adamw_against_torch_optim_adamw(order, lr, b2, eps):
+    """The oracle's AdamW against torch.optim.AdamW (the library routine, run
+    in float64 as the exact reference) over 30 steps of random bf16 gradients
+    spanning four decades.  Two mathematical identities map the page's step
+    onto torch's: torch adds eps to sqrt(v)/sqrt(1-beta2^t), so the folded
+    form's eps equals torch's eps times sqrt(1-beta2^t); and the page's order
+    p <- (p - sigma*q)*delta equals torch's decay-first step run with learning
+    rate lr*delta and weight decay wd/delta.  What remains is the fp32 master's
+    own rounding: per step, delta rounded to binary32, the product and the
+    difference (up to 1.5 ulp of |p|) and a few ulps of the step itself; the
+    bound below allows 2 ulps of |p| and 2^-22 * 8 lr per step and element."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0xADA + int(1e4 * lr))
+    n, T, b1, wd = 4096, 30, 0.9, 0.1
+    p0 = rng.normal(0, 0.5, n).astype(np.float32)
+    x = p0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    delta = 1.0 - lr * wd
+    variant = oracle.DECAY_FIRST if order == "decay_first" else 0
+    t_lr, t_wd = (lr, wd) if variant else (lr * delta, wd / delta)
+    tp = torch.tensor(p0.astype(np.float64), requires_grad=True)
+    opt = torch.optim.AdamW([tp], lr=t_lr, betas=(b1, b2), eps=eps, weight_decay=t_wd, foreach=False)
+    pmax = np.abs(p0).astype(np.float64)
+    for t in range(1, T + 1):
+        gb = oracle.f32_to_bf16(rng.normal(0, 1, n).astype(np.float32) * np.float32(10.0 ** -rng.integers(0, 4)))
+        hp = dict(lr=lr, beta1=b1, beta2=b2, eps=eps * math.sqrt(1 - b2 ** t), weight_decay=wd,
+                  max_norm=math.inf, step=t)
+        oracle.step([gb], x, m, v, oracle.f32_to_bf16(x), hp, np.zeros(1), 0, variant=variant)
+        tp.grad = torch.tensor(oracle.bf16_to_f32(gb).astype(np.float64))
+        opt.step()
+        ref = tp.detach().numpy()
+        pmax = np.maximum(pmax, np.abs(ref))
+        bound = t * 2.0 ** -22 * (pmax + 8 * lr)
+        err = np.abs(x.astype(np.float64) - ref)
+        assert (err <= bound).all(), (order, t, float((err / bound).max()))
+    st = opt.state[tp]
+    # the second moment is positive: a plain relative bound holds for it
+    vv = st["exp_avg_sq"].numpy()
+    assert np.max(np.abs(v - vv) / vv) < 1e-5
+    # the first moment, in units of the gradient scale it averages
+    assert np.max(np.abs(m - st["exp_avg"].numpy()) / np.sqrt(vv)) < 1e-5
+
+
 def test_torch_clip_convention_against_torch():
     """The torch clip variant reproduces torch.nn.utils.clip_grad_norm_'s
     coefficient (max_norm / (norm + 1e-6), clamped at 1; fp64 gradients)."""
