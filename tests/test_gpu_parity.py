@@ -1036,12 +1036,21 @@ def test_random_configurations(env, case):
                       lambda t: scale * (1 + t), max_norm=max_norm, ranks=[r], variant=variant)
 
 
+# (sum only, compatibility variant) of each random-cut case
+BUCKET_VARIANTS = [(False, 0), (False, oracle.G_BF16 | oracle.DECAY_FIRST), (True, 0),
+                   (True, oracle.CLIP_EPS | oracle.G_BF16)]
+
+
 @pytest.mark.parametrize("case", range(4))
 def test_bucketed_reduction_random_cuts(env, case):
     """Buckets cut at random points of the shard (most not on 8-element or
     tile boundaries, so both the vector and the element paths run), reduced
-    in a random order: the state equals the oracle's step."""
+    in a random order, with the sum kept or averaged and with compatibility
+    variants: the state equals the oracle's step."""
     torch, dev = env
+    sum_only, variant = BUCKET_VARIANTS[case]
+    flags = z.STORE_G | (z.SUM_ONLY if sum_only else 0) | lib_flags(variant)
+    rflags = flags & (z.STORE_G | z.SUM_ONLY | z.G_BF16)    # what the bucket reduce takes
     rng = np.random.default_rng(0xB0C4 + case)
     W = int(rng.choice([2, 4, 8]))
     numels = RAGGED
@@ -1058,19 +1067,23 @@ def test_bucketed_reduction_random_cuts(env, case):
         ranges = list(zip(cuts[:-1], cuts[1:]))
         parts = torch.zeros(len(ranges), dtype=torch.float64, device=dev)
         G = replicas(0xE200 + case, t, W, N, 0.3, outlier_pct=1)
-        part = np.array([oracle.sumsq(oracle.shard_reduce([g[q0:q0 + n] for g in G]))
-                         for q0, n in (z.shard_range(N, W, q) for q in range(W))])
+        def reduced(q0, n):
+            gr = oracle.shard_reduce([g[q0:q0 + n] for g in G], average=not sum_only)
+            return oracle.round_to_bf16(gr) if variant & oracle.G_BF16 else gr
+
+        part = np.array([oracle.sumsq(reduced(q0, n)) for q0, n in (z.shard_range(N, W, q) for q in range(W))])
         for k in rng.permutation(len(ranges)):
             lo, hi = (int(x) for x in ranges[k])
             bucket = [to_dev_u16(torch, g[sh.begin + lo:sh.begin + hi].copy(), dev) for g in G]
-            z.mta_reduce_range(bucket, sh.plan, lo, hi, parts[k:k + 1], flags=z.STORE_G, ws=ws)
+            z.mta_reduce_range(bucket, sh.plan, lo, hi, parts[k:k + 1], flags=rflags, ws=ws)
         rsd.copy_(torch.from_numpy(part))
         z.partials_sum(parts, len(ranges), rsd[r:r + 1])
         gd = [to_dev_u16(torch, g, dev) for g in G]
-        z.mta_update(gd, sh.begin, sh.plan, hp_at(t), rsd, W, flags=z.STORE_G, ws=ws)
+        z.mta_update(gd, sh.begin, sh.plan, hp_at(t), rsd, W, flags=flags, ws=ws)
         torch.cuda.synchronize()
         assert rel_close(rsd[r].item(), part[r], NORM_TOL)
-        oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), part.copy(), r)
+        oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), part.copy(), r,
+                    average=not sum_only, variant=variant)
     master, m, v, p = sh.gather()
     assert_f32_equal(master, o.master, "master")
     assert_f32_equal(m, o.m, "m")
