@@ -25,6 +25,7 @@ Modes:
   python bench.py [--steps K] [--warmup W] [--config C2]    the benchmark line
   python bench.py --pmc-run                                   short run for rocprofv3 --pmc
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR OUT     counter summary for profiles/
+                 [--pmc-also KERNEL]                          (and of another kernel of the step)
   python bench.py --summarize-kt KT_DIR OUT                   kernel-trace summary for profiles/
 """
 from __future__ import annotations
@@ -279,10 +280,12 @@ def read_pmc_dir(d):
     return {k: list(v.values()) for k, v in out.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL):
+def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL, also=()):
     """Median FETCH_SIZE / WRITE_SIZE per dispatch of `kernel`, scaled by what
     the same counters read for a torch.neg over CALIB_BYTES (a plain copy:
-    CALIB_BYTES read, CALIB_BYTES written), appended to out_path."""
+    CALIB_BYTES read, CALIB_BYTES written), appended to out_path; the same for
+    each kernel whose name contains one of `also` (e.g. the step's reduce,
+    named with its template arguments), as also_* lines."""
     fetch, write = read_pmc_dir(fetch_dir), read_pmc_dir(write_dir)
 
     def pick(d, key):
@@ -309,6 +312,14 @@ def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL):
              f"WRITE_SIZE {stt.median(vw):.1f} KiB",
              f"dominant_fetch_bytes = {fb:.0f}",
              f"dominant_write_bytes = {wb:.0f}"]
+    for name in also:
+        ka, va = pick(fetch, name)
+        _, wa = pick(write, name)
+        lines += [f"also_kernel = {name}",
+                  f"# raw per dispatch (median of {len(va)}): FETCH_SIZE {stt.median(va):.1f} KiB, "
+                  f"WRITE_SIZE {stt.median(wa):.1f} KiB",
+                  f"also_fetch_bytes = {stt.median(va) * 1024 * f_scale:.0f}",
+                  f"also_write_bytes = {stt.median(wa) * 1024 * w_scale:.0f}"]
     with open(out_path, "a") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -421,11 +432,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--pmc-also", action="append", default=[], metavar="KERNEL",
+                    help="with --summarize-pmc: also summarize kernels whose name contains this")
     ap.add_argument("--summarize-kt", nargs=2, metavar=("KT_DIR", "OUT"))
     a = ap.parse_args()
 
     if a.summarize_pmc:
-        summarize_pmc(*a.summarize_pmc)
+        summarize_pmc(*a.summarize_pmc, also=a.pmc_also)
         return 0
     if a.summarize_kt:
         summarize_kt(*a.summarize_kt)
