@@ -301,13 +301,49 @@ __device__ __forceinline__ double block_sum(double x)
     return t;
 }
 
+// The sum-of-squares pass that stores nothing (the first pass of the
+// recompute design) over whole tiles when there are few slices: one tile of
+// WS slices is only 8*WS bytes per lane, too little in flight to keep HBM
+// busy, so the loads of U tiles (U*WS <= 8 slice words per lane) are issued
+// together.  The tiles are then reduced and squared in tile order, so acc
+// takes the same sequence of values as one tile at a time.  Returns the
+// first tile not processed.
+template <int WS, int U>
+__device__ __forceinline__ int64_t norm_tiles(const Reduce& r, int64_t t, int64_t end, int64_t step, double& acc)
+{
+    for (; t + (U - 1) * step < end; t += U * step) {
+        Raw x[U][WS];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+#pragma unroll
+            for (int w = 0; w < WS; ++w) x[k][w] = ld_raw(r.gp.p[w] + (t + k * step) * kTile);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float sv[8];
+            raw_init(sv, x[k][0]);
+#pragma unroll
+            for (int w = 1; w < WS; ++w) raw_add(sv, x[k][w]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                sv[j] = average(r, sv[j]);
+                acc = fma((double)sv[j], (double)sv[j], acc);
+            }
+        }
+    }
+    return t;
+}
+
 // ------------------------------------------------------------- phase 1
 // W-slice reduce over the workgroup's tiles; optionally stores g (GNT: with
 // the non-temporal hint, for g larger than the MALL) and accumulates this
 // lane's fp64 sum of squares.  Full tiles run a software pipeline: tile t's g
 // is stored only after tile t+step's loads are issued.  A ragged last tile
-// takes the element path.
-template <bool VEC, bool STORE, bool NORM, bool GNT>
+// takes the element path.  FEW (1..4, sum of squares only): the launch has
+// exactly that many slices and the whole tiles go through norm_tiles (a
+// separate instantiation, so that its registers do not lower the occupancy
+// of the general kernel).
+template <bool VEC, bool STORE, bool NORM, bool GNT, int FEW>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len, float* __restrict__ g_out,
                                                           double* __restrict__ partials, int split)
 {
@@ -316,6 +352,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len,
     const Units u = xcd_units(ntiles, split);
     int64_t t = u.lo;
     const int64_t full_end = VEC ? (u.hi < len / kTile ? u.hi : len / kTile) : u.lo;
+    static_assert(FEW == 0 || (VEC && !STORE && NORM && FEW <= 4), "few-slice pass: vector, sum of squares only");
+    if constexpr (FEW > 0) t = norm_tiles<FEW, 8 / (FEW == 3 ? 4 : FEW)>(r, t, full_end, u.step, acc);
     if (VEC && t < full_end) {
         float sp[8];                // the previous tile's g, stored after the next tile's loads
         int64_t tp = t;
@@ -782,7 +820,15 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, d
     const dim3 grid(nblocks);
     const bool store = g_out != nullptr, norm = partials != nullptr;
     hipError_t e;
-#define Z1_REDUCE(V, ST, NO, NT) e = run(reduce_kernel<V, ST, NO, NT>, grid, s, r, len, g_out, partials, split)
+    if (vec && norm && !store && r.W <= 4) {
+        switch (r.W) {
+        case 1: return run(reduce_kernel<true, false, true, false, 1>, grid, s, r, len, g_out, partials, split);
+        case 2: return run(reduce_kernel<true, false, true, false, 2>, grid, s, r, len, g_out, partials, split);
+        case 3: return run(reduce_kernel<true, false, true, false, 3>, grid, s, r, len, g_out, partials, split);
+        default: return run(reduce_kernel<true, false, true, false, 4>, grid, s, r, len, g_out, partials, split);
+        }
+    }
+#define Z1_REDUCE(V, ST, NO, NT) e = run(reduce_kernel<V, ST, NO, NT, 0>, grid, s, r, len, g_out, partials, split)
 #define Z1_REDUCE_V(V)                                                  \
     do {                                                                \
         if (store && norm) {                                            \
