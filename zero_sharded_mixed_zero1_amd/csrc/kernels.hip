@@ -30,9 +30,11 @@
 // fp64, so fma(x, x, acc) rounds exactly like acc + x*x).
 //
 // Determinism: every workgroup owns a fixed set of tiles, every lane adds its
-// own elements in a fixed order, and partial sums are combined by a fixed tree
-// (wave butterfly, then the four waves in order), so a rerun with the same
-// launch shape reproduces every bit, including the norm.
+// own elements in a fixed order, a workgroup's lanes are combined by a fixed
+// tree (wave butterfly, then the four waves in order) and the workgroups'
+// partials by another (finalize_kernel: strided lane sums, then an LDS
+// halving tree), so a rerun with the same launch shape reproduces every bit,
+// including the norm.
 #include <hip/hip_cooperative_groups.h>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
