@@ -28,7 +28,11 @@ def test_library_exports_every_declared_symbol():
     L = z.lib()
     for n in names:
         assert hasattr(L, n), f"libzero1.so does not export {n}"
-    assert z.abi_version() == 3
+    # header, library and binding agree on the ABI version
+    src = open(os.path.join(ROOT, "include", "zero1.h")).read()
+    header = int(re.search(r"#define ZERO1_ABI_VERSION (\d+)", src).group(1))
+    from zero_sharded_mixed_zero1_amd import binding
+    assert z.abi_version() == header == binding.ABI_VERSION
 
 
 def test_oracle_and_synth_libraries_load():

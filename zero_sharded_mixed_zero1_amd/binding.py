@@ -23,6 +23,9 @@ DECAY_FIRST = 0x20
 CLIP_EPS = 0x40
 G_BF16 = 0x80
 MAX_W = 128
+# the layout of the structures below and the signatures set in lib(); a
+# library that reports another ZERO1_ABI_VERSION is refused at load time
+ABI_VERSION = 3
 
 P = ctypes.c_void_p
 i64 = ctypes.c_int64
@@ -95,6 +98,9 @@ def lib():
         L = ctypes.CDLL(lib_path)
         L.zero1_abi_version.argtypes = []
         L.zero1_abi_version.restype = i32
+        if L.zero1_abi_version() != ABI_VERSION:
+            raise ImportError(f"{lib_path} has ABI version {L.zero1_abi_version()}, this binding expects "
+                              f"{ABI_VERSION}: rebuild the library with __graft_entry__.build()")
         L.zero1_last_error.argtypes = []
         L.zero1_last_error.restype = ctypes.c_char_p
         L.zero1_status_string.argtypes = [i32]
