@@ -196,13 +196,14 @@ def hp(cfg, t):
 
 # ---------------------------------------------------------------------- the step
 def run_steps(z, cfg, st, flags, k0, k1, events=None):
-    """Steps k0..k1-1 (t = k+1), rotating through the copies.  With the default
-    design a step is one zero1_mta_step call (a single launch when the shard
-    fits on chip); with an explicit two-phase design it is zero1_mta_reduce +
-    zero1_mta_update.  events[i] = (start, end) pairs: for the two-phase step
-    the reduce kernel's and the update kernel's own (zero1_time_next_launch:
-    stamped by each kernel's dispatch, no markers around it); for the single
-    launch, stream markers around the whole call."""
+    """Steps k0..k1-1 (t = k+1), rotating through the copies.  A step is one
+    zero1_mta_step call (for the two-phase designs its reduce, finalize and
+    update launches; the single launch when ONCHIP is asked for).  With
+    events (events[i] = (start, end) pairs) a two-phase step is made as its two
+    calls instead, zero1_mta_reduce + zero1_mta_update, so that the reduce
+    kernel and the update kernel each stamp their own pair
+    (zero1_time_next_launch: from the kernel's dispatch, no markers around
+    it); the single launch gets stream markers around the whole call."""
     W, rank = st["W"], st["rank"]
     copies = st["copies"]
     two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
@@ -210,12 +211,12 @@ def run_steps(z, cfg, st, flags, k0, k1, events=None):
         c = copies[k % len(copies)]
         h = hp(cfg, k + 1)
         ev = events[k - k0] if events is not None else None
-        if two_phase:
-            if ev:
-                z.time_next_launch(*ev[0])
+        if two_phase and not ev:
+            z.mta_step(c.grads, c.begin, c.plan, h, c.rsd, W, rank, flags=flags, ws=c.ws)
+        elif two_phase:
+            z.time_next_launch(*ev[0])
             z.mta_reduce(c.grads, c.begin, c.plan, c.rsd[rank:rank + 1], flags=flags, ws=c.ws)
-            if ev:
-                z.time_next_launch(*ev[1])
+            z.time_next_launch(*ev[1])
             z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
         else:
             if ev:
