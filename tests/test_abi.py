@@ -332,3 +332,50 @@ def test_bench_entry_points_and_gpu_count_contract():
                          text=True, timeout=120)
     assert out.returncode == 2 and "ONE GPU" in out.stderr, (out.returncode, out.stderr)
     assert out.stdout == ""
+
+
+def test_profile_summaries_from_counter_and_trace_files(tmp_path):
+    """The profile summarizers: counter bytes per dispatch scaled by the plain
+    copy's reading, the bench's traffic read back only while the kernel source
+    hash matches, and kernel-trace statistics split by grid size."""
+    import bench
+    fetch, write = tmp_path / "fetch", tmp_path / "write"
+    for d, counts in ((fetch, {"upd": [100.0, 102.0, 101.0], "red": [40.0, 40.0, 40.0], "neg": [524288.0]}),
+                      (write, {"upd": [70.0, 70.0, 70.0], "red": [10.0, 12.0, 11.0], "neg": [1048576.0]})):
+        (d / "x").mkdir(parents=True)
+        names = {"upd": "void z1::adamw_mta_kernel<true, 0, false>(float const*)",
+                 "red": "void z1::reduce_kernel<true, true, true, false, 0>(z1::Reduce)",
+                 "neg": "void at::native::neg_kernel_impl(float)"}
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        disp = 0
+        for key, vals in counts.items():
+            for v in vals:
+                disp += 1
+                # two rows (e.g. two counter instances) of one dispatch add up
+                rows.append(f'{disp},"{names[key]}",C,{v / 2}')
+                rows.append(f'{disp},"{names[key]}",C,{v / 2}')
+        (d / "x" / "pmc_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    out = tmp_path / "summary.txt"
+    bench.summarize_pmc(str(fetch), str(write), str(out), also=["reduce_kernel<true, true, true, false, 0>"])
+    kv = dict(l.split(" = ", 1) for l in out.read_text().splitlines() if " = " in l and not l.startswith("#"))
+    # fetch scale: 1 GiB / (524288 KiB) = x2; write scale x1; medians 101 / 70 and 40 / 11 KiB
+    assert int(kv["dominant_fetch_bytes"]) == 101 * 1024 * 2 and int(kv["dominant_write_bytes"]) == 70 * 1024
+    assert int(kv["also_fetch_bytes"]) == 40 * 1024 * 2 and int(kv["also_write_bytes"]) == 11 * 1024
+    assert bench.traffic_from_summary(str(out), bench.UPDATE_KERNEL) == 101 * 2048 + 70 * 1024
+    stale = tmp_path / "stale.txt"
+    stale.write_text(out.read_text().replace(bench.kernel_source_hash(), "0" * 16))
+    assert bench.traffic_from_summary(str(stale), bench.UPDATE_KERNEL) is None
+    # kernel trace: two grids of one kernel are reported apart
+    kt = tmp_path / "kt" / "x"
+    kt.mkdir(parents=True)
+    rows = ["Kernel_Name,Grid_Size_X,Workgroup_Size_X,Start_Timestamp,End_Timestamp"]
+    for i, (grid, dur) in enumerate([(2048, 50000), (2048, 52000), (768, 9000)]):
+        rows.append(f'"void z1::(anonymous namespace)::reduce_kernel<true>(z1::Reduce)",{grid * 256},256,'
+                    f'{1000 * i},{1000 * i + dur}')
+    (kt / "kt_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    kout = tmp_path / "kt.txt"
+    bench.summarize_kt(str(tmp_path / "kt"), str(kout))
+    lines = [l for l in kout.read_text().splitlines() if l.startswith("reduce_kernel")]
+    assert len(lines) == 2
+    cols = [[c.strip() for c in l.split("|")] for l in lines]
+    assert cols[0][1:4] == ["2048", "2", "51.00"] and cols[1][1:4] == ["768", "1", "9.00"]
