@@ -170,27 +170,23 @@ __device__ __forceinline__ void st8_g(float* p, const float (&x)[8])
 
 // g kept for the update to re-read (small enough for the MALL) is stored
 // through a buffer descriptor with the sc1 policy bit rather than a plain
-// store: measured ~3 us less per reduce at the GPT-2-small W=8 shard, with
+// store: measured ~2.5 us less per reduce at the GPT-2-small W=8 shard, with
 // the same update time (the lines leave L2 as they are written instead of
-// waiting, dirty, for the write-back at the end of the kernel).  The
-// descriptor covers g_out's len elements (host: len * 4 < 2^31), so an
-// offset is a 32-bit byte count.
+// waiting, dirty, for the write-back at the end of the kernel).  One
+// descriptor per tile (base = the tile, 8 KiB), so offsets stay small for any
+// shard size.
 constexpr int kBufSc1 = 16;                   // cache-policy operand of buffer stores: sc1
 constexpr int kBufDword3 = 0x00020000;        // gfx9 buffer descriptor word 3 (raw, untyped)
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t g_rsrc(float* g_out, int64_t len)
+// The lane's 8 values of the tile that starts at `tile`.
+__device__ __forceinline__ void st8_g_sc1(float* tile, const float (&x)[8])
 {
-    return __builtin_amdgcn_make_buffer_rsrc(g_out, 0, (int)(len * 4), kBufDword3);
-}
-
-// The lane's 8 values of the tile starting at element e of g_out.
-__device__ __forceinline__ void st8_g_sc1(__amdgpu_buffer_rsrc_t rs, int64_t e, const float (&x)[8])
-{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tile, 0, kTile * 4, kBufDword3);
     const int a = quad_a();
     const f32x4 u = {x[0], x[1], x[2], x[3]};
     const f32x4 w = {x[4], x[5], x[6], x[7]};
-    __builtin_amdgcn_raw_buffer_store_b128(u, rs, (int)((e + a) * 4), 0, kBufSc1);
-    __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)((e + a + 256) * 4), 0, kBufSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs, a * 4, 0, kBufSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(w, rs, (a + 256) * 4, 0, kBufSc1);
 }
 
 __device__ __forceinline__ void ld8_g(const float* p, float (&x)[8])
@@ -379,8 +375,6 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len,
     const Units u = xcd_units(ntiles, split);
     int64_t t = u.lo;
     const int64_t full_end = VEC ? (u.hi < len / kTile ? u.hi : len / kTile) : u.lo;
-    __amdgpu_buffer_rsrc_t grs;
-    if constexpr (STORE && !GNT) grs = g_rsrc(g_out, len);
     static_assert(FEW == 0 || (VEC && !STORE && NORM && FEW <= 4), "few-slice pass: vector, sum of squares only");
     if constexpr (FEW > 0) t = norm_tiles<FEW, 8 / (FEW == 3 ? 4 : FEW)>(r, t, full_end, u.step, acc);
     if (VEC && t < full_end) {
@@ -395,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len,
             float s[8];
             reduce8(r, t * kTile, s, [&] {
                 if constexpr (STORE && GNT) st8_g<true>(g_out + tp * kTile, sp);
-                if constexpr (STORE && !GNT) st8_g_sc1(grs, tp * kTile, sp);
+                if constexpr (STORE && !GNT) st8_g_sc1(g_out + tp * kTile, sp);
             });
             if constexpr (NORM) {
 #pragma unroll
@@ -406,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len,
             tp = t;
         }
         if constexpr (STORE && GNT) st8_g<true>(g_out + tp * kTile, sp);
-        if constexpr (STORE && !GNT) st8_g_sc1(grs, tp * kTile, sp);
+        if constexpr (STORE && !GNT) st8_g_sc1(g_out + tp * kTile, sp);
     }
     for (; t < u.hi; t += u.step) {
         const int64_t base = t * kTile;
@@ -850,7 +844,6 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, d
 {
     const dim3 grid(nblocks);
     const bool store = g_out != nullptr, norm = partials != nullptr;
-    if (store && len >= ((int64_t)1 << 29)) g_nt = true;   // the sc1 store's descriptor spans < 2^31 bytes
     hipError_t e;
     if (vec && norm && !store && r.W <= 4) {
         switch (r.W) {
