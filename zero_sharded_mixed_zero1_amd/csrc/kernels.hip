@@ -11,7 +11,8 @@
 //     non-temporal hint (global_load/store ... nt): streaming data should not
 //     displace anything in L2/MALL.  On MI355X this is worth ~1.5-2x over
 //     plain accesses for these kernels.  g, written by the reduce and read
-//     back by the update, keeps the default policy while it fits the MALL.
+//     back by the update, is stored with the sc1 policy and read with the
+//     default one while it fits the MALL.
 //   * Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs
 //     on XCD b % 8), and each XCD has its own L2 and address-translation
 //     caches.  So the tiles are split into 8 contiguous eighths and XCD x's
@@ -74,9 +75,10 @@ __device__ __forceinline__ void st_nt(T* p, T v) { __builtin_nontemporal_store(v
 // The reduced gradient g (store-g design) is written by one kernel and read
 // back by the next.  The update reads it with the default cache policy, so a
 // g that fits in the 256 MB MALL is re-read mostly from there (GPT-2 small
-// W=8 shard: update kernel 82 -> 75 us); the reduce stores it with the default
-// policy for such sizes and with the non-temporal hint (NT) for larger ones,
-// where it cannot stay resident anyway.
+// W=8 shard: update kernel 82 -> 75 us); the reduce stores such a g with sc1
+// buffer stores (st8_g_sc1 below; a ragged tail with plain stores) and a
+// larger one with the non-temporal hint (NT), where it cannot stay resident
+// anyway.
 template <bool NT = false, typename T>
 __device__ __forceinline__ T ld_g(const T* p)
 {
