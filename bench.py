@@ -6,36 +6,48 @@ gradient slices (fp32, rank order, / W), this rank's fp64 sum of squares, the
 global-norm clip, AdamW (update, then decay) on the fp32 master/m/v, and the
 bf16 parameter write-back over the ragged per-tensor list (multi-tensor apply).
 
-Default workload: the GPT-2 small tensor list (148 tensors, 124,439,808
-parameters) cut into W=8 ZeRO-1 shards; rank 4's 15,554,976-parameter shard
-(31 pieces).  All inputs are synthetic (seeded) and resident in HBM before the
-timed region.  The other ranks' partial sums of squares are computed once
-before timing (they are what a multi-GPU run would exchange mid-step).
+Headline workload: the full AdamW step of a dense 7e9-parameter model at W=1
+(no reduction; fp32 master, m, v: 16 B/param of state, 28 B/param moved per
+step), the largest configuration that fits one GPU.  The same line carries
+`per_config`: the other workloads (flat 2^20 W=4, GPT-2 small W=8, dense 7.5e9
+W=64, Llama-7B W=8, the 7e9 step with bf16 m, v), each timed the same way.
+All inputs are synthetic (seeded) and resident in HBM before any timed region.
+For the workloads whose other ranks' gradients are not resident, the other
+ranks' partial sums of squares are 0 (the norm is this shard's own).
 
-Memory: by default every array of the step sits in one allocation laid out by
-zero1_arena_plan (the update's five streams 40 GiB apart; HBM serves them
-faster than arrays packed together); --layout packed allocates each array on
-its own.
+Every workload is measured in two memory layouts: "arena" (every array of the
+step in one allocation laid out by zero1_arena_plan: the update's five streams
+40 GiB apart) and "packed" (one torch allocation per array).  The headline
+`value` is the arena figure; the packed one is reported beside it.
+
+Per kernel the line gives the algorithmic bytes over its own duration (HIP
+events stamped by the kernel's dispatch), the bytes the design moves, and a
+calibrated ceiling: the time of a kernel that moves exactly the same streams
+with the same access pattern and placement and computes nothing
+(libzero1_calib.so).
 
 Prints ONE JSON line.  Metric: shard parameters updated per second; the
 algorithmic HBM traffic is (2W+26) bytes per parameter (W bf16 gradient reads,
-fp32 master/m/v read + write, bf16 parameter write).
+fp32 master/m/v read + write, bf16 parameter write; 2W+18 with bf16 m, v).
 
 Modes:
-  python bench.py [--steps K] [--warmup W] [--config C2]    the benchmark line
-  python bench.py --pmc-run                                   short run for rocprofv3 --pmc
-  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR OUT     counter summary for profiles/
-                 [--pmc-also KERNEL]                          (and of another kernel of the step)
-  python bench.py --summarize-kt KT_DIR OUT                   kernel-trace summary for profiles/
+  python bench.py [--steps K] [--warmup W]                     the benchmark line
+  python bench.py --config C4 [--layout arena] --no-per-config one workload only
+  python bench.py --calibrate                                  plain read/write/copy rates
+  python bench.py --pmc-run --config C                         short run for rocprofv3 --pmc
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR OUT      counter summary for profiles/
+  python bench.py --summarize-kt KT_DIR OUT                    kernel-trace summary for profiles/
 """
 from __future__ import annotations
 
 import argparse
-import glob
 import csv
+import ctypes
+import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -44,10 +56,19 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 UPDATE_KERNEL = "adamw_mta_kernel"
-ONCHIP_KERNEL = "onchip_step_kernel"
 REDUCE_KERNEL = "reduce_kernel"
 CALIB_BYTES = 1 << 30          # the plain copy used to scale the PMC byte counters
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_mta_kernel_gpt2small_w8_pmc.txt")
+HEADLINE = "C5a"
+PER_CONFIG = ("C1", "C2", "C3", "C4", "C5b")
+# profile summaries are named for the workload they cover
+WORKLOAD_TAG = {"C1": "flat1m_w4", "C2": "gpt2small_w8", "C3": "dense7p5b_w64", "C4": "llama7b_w8",
+                "C5a": "dense7b_w1", "C5b": "dense7b_w1_bf16mv"}
+# timed steps per layout of the small workloads (their steps take microseconds)
+MIN_STEPS = {"C1": 400, "C2": 200}
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -65,13 +86,73 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def pmc_summary_path(name):
+    return os.path.join(ROOT, "profiles", f"zero1_step_{WORKLOAD_TAG[name]}_pmc.txt")
+
+
+# ---------------------------------------------------------------------- calibration kernels
+_cal = None
+
+
+def cal_lib():
+    global _cal
+    if _cal is None:
+        path = os.path.join(ROOT, "zero_sharded_mixed_zero1_amd", "libzero1_calib.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built: run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.zcal_stream.argtypes = [P, P, i32, P, P, i32, i64, i32, i32, P, P]
+        L.zcal_stream.restype = i32
+        _cal = L
+    return _cal
+
+
+def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream):
+    """One calibration pass: rd/wr are [(device address, bytes per element)];
+    every stream must hold n_tiles * 2048 elements from its address."""
+    R, Wn = len(rd), len(wr)
+    rp = (ctypes.c_void_p * max(R, 1))(*[a for a, _ in rd])
+    rb = (ctypes.c_int * max(R, 1))(*[b for _, b in rd])
+    wp = (ctypes.c_void_p * max(Wn, 1))(*[a for a, _ in wr])
+    wb = (ctypes.c_int * max(Wn, 1))(*[b for _, b in wr])
+    st = cal_lib().zcal_stream(rp, rb, R, wp, wb, Wn, n_tiles, grid, split, sink, stream)
+    if st != 0:
+        raise RuntimeError(f"zcal_stream failed with status {st}")
+
+
+def timed_passes(torch, fn, reps):
+    """Median duration (ms) of fn() over reps launches, each between HIP events
+    on torch's current stream (the stream fn launches on)."""
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return statistics.median(out)
+
+
+def launch_shape(units, cus, per_cu, big_split):
+    """The library's grid for a pass over `units` tiles (internal grid_for):
+    per_cu > 0 caps the grid at per_cu * CUs; a multiple of 8."""
+    cap = min(cus * per_cu if per_cu > 0 else units, 8192)
+    n = min(units, cap)
+    if n > 8:
+        n = (n + 7) // 8 * 8
+    n = max(n, 1)
+    return n, (8 if big_split(units, n) else 1)
+
+
 # ---------------------------------------------------------------------- setup
 class Copy:
     """One independent copy of everything a step touches (rotated through so
     that consecutive steps do not find each other's data in the 256 MB MALL)."""
 
 
-def setup(torch, cfg, design_flags, n_copies, dev, layout="arena", arena_all=False, arena_offset=0):
+def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
     """Every array of n_copies independent copies of one rank's step, resident
     in HBM.  layout "arena": one allocation laid out by zero1_arena_plan (the
     update's five streams 40 GiB apart, the gradient buffers packed after
@@ -116,12 +197,7 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena", arena_all=Fal
                 info.update(layout="packed", arena_refused="the rotated copies do not fit in the arena's gaps")
         layout = info["layout"]
     if layout == "arena":
-        base = (int(arena_offset) >> 21) << 21
-        if arena_all:   # the arena takes all free memory (less 8 GB), as a preallocating allocator would
-            if base + total > cap:
-                raise SystemExit("arena: the offset layout does not fit in the free memory")
-            total = max(base + total, cap)
-        arena = torch.empty(total, dtype=torch.uint8, device=dev)[base:]
+        arena = torch.empty(total, dtype=torch.uint8, device=dev)
         info.update(arena_bytes=total, spacing_gib=L.spacing / (1 << 30))
         spans = []
 
@@ -157,6 +233,7 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena", arena_all=Fal
             # only this rank's W slices exist (their global flat indices start at begin)
             cp.begin = 0
         cp.grads = bufs
+        cp.shard_params = cp.params[begin - p_lo:begin - p_lo + S]
         synth.fill_f32_(cp.master, synth.master_key(cfg.seed), begin, cfg.master_sigma)
         cp.m.zero_()
         cp.v.zero_()
@@ -190,77 +267,215 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena", arena_all=Fal
     return dict(W=W, rank=rank, N=N, S=S, begin=begin, pieces=len(pieces_l), copies=copies, info=info)
 
 
-def hp(cfg, t):
-    return cfg.hparams(t)
-
-
 # ---------------------------------------------------------------------- the step
 def run_steps(z, cfg, st, flags, k0, k1, events=None):
     """Steps k0..k1-1 (t = k+1), rotating through the copies.  A step is one
-    zero1_mta_step call (for the two-phase designs its reduce, finalize and
-    update launches; the single launch when ONCHIP is asked for).  With
-    events (events[i] = (start, end) pairs) a two-phase step is made as its two
+    zero1_mta_step call (its reduce, finalize and update launches).  With
+    events (events[i] = (start, end) pairs) each step is made as its two
     calls instead, zero1_mta_reduce + zero1_mta_update, so that the reduce
     kernel and the update kernel each stamp their own pair
-    (zero1_time_next_launch: from the kernel's dispatch, no markers around
-    it); the single launch gets stream markers around the whole call."""
+    (zero1_time_next_launch: from the kernel's dispatch, no markers around it)."""
     W, rank = st["W"], st["rank"]
     copies = st["copies"]
-    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
     for k in range(k0, k1):
         c = copies[k % len(copies)]
-        h = hp(cfg, k + 1)
-        ev = events[k - k0] if events is not None else None
-        if two_phase and not ev:
+        h = cfg.hparams(k + 1)
+        if events is None:
             z.mta_step(c.grads, c.begin, c.plan, h, c.rsd, W, rank, flags=flags, ws=c.ws)
-        elif two_phase:
+        else:
+            ev = events[k - k0]
             z.time_next_launch(*ev[0])
             z.mta_reduce(c.grads, c.begin, c.plan, c.rsd[rank:rank + 1], flags=flags, ws=c.ws)
             z.time_next_launch(*ev[1])
             z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
-        else:
-            if ev:
-                ev[0][0].record()
-            z.mta_step(c.grads, c.begin, c.plan, h, c.rsd, W, rank, flags=flags, ws=c.ws)
-            if ev:
-                ev[0][1].record()
+
+
+def ceilings(torch, z, cfg, st, store_g, cus):
+    """Calibrated ceilings of the two kernels of the step: the same streams
+    (copy 0's arrays, at their addresses), moved with the same access pattern
+    and launch shape by a kernel that computes nothing.  Run after the timed
+    passes (it overwrites the arrays)."""
+    W, S = st["W"], st["S"]
+    c = st["copies"][0]
+    mvb = 2 if cfg.mv_bf16 else 4
+
+    def al(addr):            # first 16-byte aligned address at or after addr
+        return (addr + 15) // 16 * 16
+
+    n_tiles = max(0, (S - 8) // 2048)
+    if n_tiles == 0:
+        return None
+    grads = [al(g.data_ptr() + 2 * c.begin) for g in c.grads]
+    state_rd = [(al(c.master.data_ptr()), 4), (al(c.m.data_ptr()), mvb), (al(c.v.data_ptr()), mvb)]
+    state_wr = state_rd + [(al(c.shard_params.data_ptr()), 2)]
+    if store_g:
+        g = al(c.ws.data_ptr() + 256 + 8 * 8192)      # the g region of the workspace
+        red_rd, red_wr = [(a, 2) for a in grads], [(g, 4)]
+        upd_rd = [(g, 4)] + state_rd
+    else:
+        red_rd, red_wr = [(a, 2) for a in grads], []
+        upd_rd = [(a, 2) for a in grads] + state_rd
+    sink = torch.zeros(8192, dtype=torch.int32, device=c.master.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    rg, rs = launch_shape(n_tiles, cus, 8, lambda u, n: u >= 16 * n)
+    ug, us = launch_shape(n_tiles, cus, 8 if n_tiles > 8192 else 0, lambda u, n: u > 8192)
+
+    def one(rd, wr, grid, split):
+        zcal_stream(rd, wr, n_tiles, grid, split, sink.data_ptr(), stream)
+
+    out = {}
+    for name, rd, wr, grid, split in (("reduce", red_rd, red_wr, rg, rs), ("update", upd_rd, state_wr, ug, us)):
+        one(rd, wr, grid, split)
+        torch.cuda.synchronize()
+        ms = timed_passes(torch, lambda: one(rd, wr, grid, split), 5)
+        nbytes = n_tiles * 2048 * (sum(b for _, b in rd) + sum(b for _, b in wr))
+        out[name] = {"ms": ms, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                     "shard_ms": ms * S / (n_tiles * 2048)}
+    return out
+
+
+def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
+    """One workload in one layout: warmup, K timed steps, K kernel-timed steps,
+    the calibrated ceilings (and, for the store-g design, the bucketed flow)."""
+    W = cfg.W
+    store_g = W > 4
+    per_copy = cfg.S * (2 * W + 26 + (4 if store_g else 0))
+    n_copies = 2 if per_copy < (1 << 30) else 1
+    design = z.STORE_G if store_g else z.RECOMPUTE_G
+    st = setup(torch, cfg, design, n_copies, dev, layout)
+    S = st["S"]
+    c0 = st["copies"][0]
+    assert z.mta_design(c0.grads, c0.begin, c0.plan, 0) == design
+    run_steps(z, cfg, st, design, 0, warmup)
+    torch.cuda.synchronize()
+    # the timed region: exactly K steps back to back, bracketed by synchronizations
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    run_steps(z, cfg, st, design, warmup, warmup + steps)
+    g1.record()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    gpu_ms = g0.elapsed_time(g1) / steps
+
+    # each kernel's own duration: the same K steps again, each as its two
+    # calls, with the reduce and the update stamped by their own dispatches
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()   # torch creates the event at its first record
+        return e
+
+    events = [((event(), event()), (event(), event())) for _ in range(steps)]
+    torch.cuda.synchronize()
+    run_steps(z, cfg, st, design, warmup + steps, warmup + 2 * steps, events)
+    torch.cuda.synchronize()
+    upd_ms = statistics.fmean(e[1][0].elapsed_time(e[1][1]) for e in events)
+    red_ms = statistics.fmean(e[0][0].elapsed_time(e[0][1]) for e in events)
+    ms = el * 1e3 / steps
+    bpp = cfg.bytes_per_param
+    fixed = 18 if cfg.mv_bf16 else 26
+    # algorithmic bytes per launch: store-g -- the reduce does the 2W gradient
+    # reads, the update the fixed bytes; recompute -- the update does every
+    # algorithmic access (it reads the slices, the state, writes the state and
+    # the parameters) and the sum-of-squares pass is design overhead
+    if store_g:
+        red_alg, red_mv = 2 * W * S, (2 * W + 4) * S
+        upd_alg, upd_mv = fixed * S, (fixed + 4) * S
+    else:
+        red_alg, red_mv = 0, 2 * W * S
+        upd_alg, upd_mv = (2 * W + fixed) * S, (2 * W + fixed) * S
+    res = {
+        "layout": st["info"], "steps": steps, "warmup": warmup, "rotated_copies": n_copies,
+        "ms_per_step": ms, "gpu_ms_per_step": gpu_ms, "params_per_s": S / (ms * 1e-3),
+        "algorithmic_GBps": bpp * S / (ms * 1e-3) / 1e9,
+        "pct_of_peak_hbm": 100.0 * bpp * S / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "moved_bytes_per_step": red_mv + upd_mv,
+        "kernels": {
+            "reduce": {"ms": red_ms, "algorithmic_bytes": red_alg, "moved_bytes": red_mv,
+                       "algorithmic_GBps": red_alg / (red_ms * 1e-3) / 1e9,
+                       "moved_GBps": red_mv / (red_ms * 1e-3) / 1e9},
+            "update": {"ms": upd_ms, "algorithmic_bytes": upd_alg, "moved_bytes": upd_mv,
+                       "algorithmic_GBps": upd_alg / (upd_ms * 1e-3) / 1e9,
+                       "moved_GBps": upd_mv / (upd_ms * 1e-3) / 1e9},
+        },
+    }
+    for k in ("reduce", "update"):
+        kk = res["kernels"][k]
+        kk["frac_of_peak"] = kk["algorithmic_GBps"] / PEAK_HBM_GBS
+        kk["traffic"] = traffic_from_summary(pmc_summary_path(cfg.name), k) if layout == "arena" else None
+    if bucketed and store_g:
+        res["bucketed"] = bucketed_timing(torch, z, cfg, st, warmup + 2 * steps, min(steps, 50))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    cal = ceilings(torch, z, cfg, st, store_g, cus)
+    if cal:
+        for k in ("reduce", "update"):
+            kk = res["kernels"][k]
+            kk["ceiling_ms"] = cal[k]["shard_ms"]
+            kk["ceiling_moved_GBps"] = cal[k]["GBps"]
+            kk["frac_of_ceiling"] = cal[k]["shard_ms"] / kk["ms"]
+        res["ceiling_ms_per_step"] = cal["reduce"]["shard_ms"] + cal["update"]["shard_ms"]
+    del st, c0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, S_total, begin, budget_s=12.0, max_steps=2000):
-    """The oracle, as it stands, on the same rank's shard (a bounded sample):
-    as many full steps as fit in about budget_s seconds of host time."""
+CPU_SAMPLE = {"C1": None, "C2": None, "C3": 1 << 20, "C4": 1 << 22, "C5a": 1 << 23, "C5b": 1 << 23}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
+def cpu_baseline(cfg, budget_s=2.0, max_steps=2000):
+    """The oracle, as it stands, on the same rank's shard (C1, C2 whole; the
+    larger shards on their first CPU_SAMPLE parameters): as many full steps
+    as fit in about budget_s seconds of host time (after one untimed step),
+    with 1 thread and with N threads (N = OMP_NUM_THREADS if set, else the
+    CPU count)."""
     import numpy as np
     import oracle
     import synth
 
     W = cfg.W
-    n = min(S_total, 16 * 1024 * 1024)     # at most 16M parameters of the shard
+    begin, end = cfg.shard
+    S = end - begin
+    n = S if CPU_SAMPLE[cfg.name] is None else min(S, CPU_SAMPLE[cfg.name])
     grads = [synth.bf16(n, synth.grad_key(cfg.seed, 1, w), begin, cfg.sigma, cfg.outlier_pct) for w in range(W)]
-    master = synth.f32(n, synth.master_key(cfg.seed), begin, cfg.master_sigma)
+    master0 = synth.f32(n, synth.master_key(cfg.seed), begin, cfg.master_sigma)
     mvd = np.uint16 if cfg.mv_bf16 else np.float32
-    m, v = np.zeros(n, mvd), np.zeros(n, mvd)
-    param = np.zeros(n, np.uint16)
-    rs = np.zeros(W)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.step(grads, master, m, v, param, hp(cfg, steps + 1), rs, cfg.rank % W)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= max_steps:
-            break
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
-    except OSError:
-        pass
-    return {"value": n * steps / el, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full oracle steps (reduce, norm, clip, AdamW, bf16) on the first {n:,} "
-                      f"parameters of the same rank's shard, W={W}, {el:.1f} s on {threads} threads",
-            "cpu": cpu, "host_cpus": os.cpu_count()}
+    n_max = min(int(os.environ.get("OMP_NUM_THREADS") or 0) or (os.cpu_count() or 1), os.cpu_count() or 1)
+    out = {}
+    for threads in (1, n_max):
+        used = oracle.threads(threads)
+        master = master0.copy()
+        m, v = np.zeros(n, mvd), np.zeros(n, mvd)
+        param = np.zeros(n, np.uint16)
+        rs = np.zeros(W)
+        # one untimed step first: it takes the page faults of the new arrays
+        oracle.step(grads, master, m, v, param, cfg.hparams(1), rs, cfg.rank % W)
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.step(grads, master, m, v, param, cfg.hparams(steps + 2), rs, cfg.rank % W)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or steps >= max_steps:
+                break
+        out[threads] = {"value": n * steps / el, "cores": used, "steps": steps, "seconds": el}
+    whole = "the whole shard" if n == S else f"the first {n:,} parameters of the shard"
+    return {"value": out[n_max]["value"], "unit": "params/s", "cores": out[n_max]["cores"], "kind": "oracle",
+            "sample": f"{out[n_max]['steps']} full oracle steps (reduce, norm, clip, AdamW, bf16) on {whole} "
+                      f"({cfg.workload}), {out[n_max]['seconds']:.1f} s on {out[n_max]['cores']} threads",
+            "single_thread": {"value": out[1]["value"], "unit": "params/s", "cores": out[1]["cores"],
+                              "sample": f"{out[1]['steps']} steps on {whole}, {out[1]['seconds']:.1f} s"},
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 # ---------------------------------------------------------------------- PMC summary
@@ -281,12 +496,11 @@ def read_pmc_dir(d):
     return {k: list(v.values()) for k, v in out.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL, also=()):
-    """Median FETCH_SIZE / WRITE_SIZE per dispatch of `kernel`, scaled by what
-    the same counters read for a torch.neg over CALIB_BYTES (a plain copy:
-    CALIB_BYTES read, CALIB_BYTES written), appended to out_path; the same for
-    each kernel whose name contains one of `also` (e.g. the step's reduce,
-    named with its template arguments), as also_* lines."""
+def summarize_pmc(fetch_dir, write_dir, out_path):
+    """Median FETCH_SIZE / WRITE_SIZE per dispatch of the step's update and
+    reduce kernels, scaled by what the same counters read for a torch.neg over
+    CALIB_BYTES (a plain copy: CALIB_BYTES read, CALIB_BYTES written),
+    appended to out_path as update_* and reduce_* lines."""
     fetch, write = read_pmc_dir(fetch_dir), read_pmc_dir(write_dir)
 
     def pick(d, key):
@@ -295,32 +509,21 @@ def summarize_pmc(fetch_dir, write_dir, out_path, kernel=UPDATE_KERNEL, also=())
                 return k, v
         raise SystemExit(f"no kernel matching {key!r} in {list(d)[:10]}")
 
-    import statistics as stt
-    kf, vf = pick(fetch, kernel)
-    _, vw = pick(write, kernel)
     _, cf = pick(fetch, "neg_kernel")
     _, cw = pick(write, "neg_kernel")
-    f_scale = (CALIB_BYTES / 1024.0) / stt.median(cf)
-    w_scale = (CALIB_BYTES / 1024.0) / stt.median(cw)
-    fb = stt.median(vf) * 1024 * f_scale
-    wb = stt.median(vw) * 1024 * w_scale
+    f_scale = (CALIB_BYTES / 1024.0) / statistics.median(cf)
+    w_scale = (CALIB_BYTES / 1024.0) / statistics.median(cw)
     lines = [f"kernel_source_hash = {kernel_source_hash()}",
-             f"dominant_kernel = {kernel}",
-             f"# {kf[:110]}",
-             f"# calibration: torch.neg over {CALIB_BYTES} B fp32 reads FETCH_SIZE {stt.median(cf):.1f} KiB "
-             f"and WRITE_SIZE {stt.median(cw):.1f} KiB; scale fetch x{f_scale:.4f}, write x{w_scale:.4f}",
-             f"# raw per dispatch (median of {len(vf)}): FETCH_SIZE {stt.median(vf):.1f} KiB, "
-             f"WRITE_SIZE {stt.median(vw):.1f} KiB",
-             f"dominant_fetch_bytes = {fb:.0f}",
-             f"dominant_write_bytes = {wb:.0f}"]
-    for name in also:
-        ka, va = pick(fetch, name)
-        _, wa = pick(write, name)
-        lines += [f"also_kernel = {name}",
-                  f"# raw per dispatch (median of {len(va)}): FETCH_SIZE {stt.median(va):.1f} KiB, "
-                  f"WRITE_SIZE {stt.median(wa):.1f} KiB",
-                  f"also_fetch_bytes = {stt.median(va) * 1024 * f_scale:.0f}",
-                  f"also_write_bytes = {stt.median(wa) * 1024 * w_scale:.0f}"]
+             f"# calibration: torch.neg over {CALIB_BYTES} B fp32 reads FETCH_SIZE {statistics.median(cf):.1f} KiB "
+             f"and WRITE_SIZE {statistics.median(cw):.1f} KiB; scale fetch x{f_scale:.4f}, write x{w_scale:.4f}"]
+    for label, key in (("update", UPDATE_KERNEL), ("reduce", REDUCE_KERNEL)):
+        kf, vf = pick(fetch, key)
+        _, vw = pick(write, key)
+        lines += [f"# {label}: {kf[:110]}",
+                  f"# raw per dispatch (median of {len(vf)}): FETCH_SIZE {statistics.median(vf):.1f} KiB, "
+                  f"WRITE_SIZE {statistics.median(vw):.1f} KiB",
+                  f"{label}_fetch_bytes = {statistics.median(vf) * 1024 * f_scale:.0f}",
+                  f"{label}_write_bytes = {statistics.median(vw) * 1024 * w_scale:.0f}"]
     with open(out_path, "a") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -330,29 +533,30 @@ def summarize_kt(kt_dir, out_path):
     """Per-kernel dispatch statistics from a rocprofv3 --kernel-trace output dir,
     split by grid size (the whole-shard reduce and the bucket reduces are the
     same kernel at different grids), appended to out_path."""
-    import statistics as stt
     rows = {}
     for f in glob.glob(os.path.join(kt_dir, "**", "*kernel_trace*.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 name = r["Kernel_Name"]
-                short = name.replace("void ", "").replace("z1::(anonymous namespace)::", "").split("(")[0]
+                short = name.replace("void ", "").replace("z1::(anonymous namespace)::", "")
+                short = short.replace("(anonymous namespace)::", "").split("(")[0]
                 grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
                 dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                 rows.setdefault((short, grid), []).append(dur)
-    lines = [f"{'kernel':<48} | {'workgroups':>10} | {'calls':>5} | {'avg_us':>8} | {'median_us':>9} | "
-             f"{'min_us':>8} | {'max_us':>8}"]
+    lines = [f"{'kernel':<48} | {'workgroups':>10} | {'calls':>5} | {'avg_us':>9} | {'median_us':>9} | "
+             f"{'min_us':>9} | {'max_us':>9}"]
     for (short, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{short[:48]:<48} | {grid:>10} | {len(d):>5} | {sum(d) / len(d):>8.2f} | "
-                     f"{stt.median(d):>9.2f} | {min(d):>8.2f} | {max(d):>8.2f}")
+        lines.append(f"{short[:48]:<48} | {grid:>10} | {len(d):>5} | {sum(d) / len(d):>9.2f} | "
+                     f"{statistics.median(d):>9.2f} | {min(d):>9.2f} | {max(d):>9.2f}")
     with open(out_path, "a") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
 def traffic_from_summary(path, kernel):
-    """Counter bytes per launch of `kernel` from the committed summary, or None
-    if the kernels changed since the counters were taken."""
+    """Counter bytes per launch of the step's `kernel` ("update" or "reduce")
+    from the committed summary, or None if the kernels changed since the
+    counters were taken."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -360,15 +564,15 @@ def traffic_from_summary(path, kernel):
         if "=" in line and not line.startswith("#"):
             k, v = (s.strip() for s in line.split("=", 1))
             kv[k] = v
-    if kv.get("kernel_source_hash") != kernel_source_hash() or kv.get("dominant_kernel") != kernel:
+    if kv.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
-        return float(kv["dominant_fetch_bytes"]) + float(kv["dominant_write_bytes"])
+        return float(kv[f"{kernel}_fetch_bytes"]) + float(kv[f"{kernel}_write_bytes"])
     except (KeyError, ValueError):
         return None
 
 
-# ---------------------------------------------------------------------- main
+# ---------------------------------------------------------------------- bucketed flow
 def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
     """The ZeRO-2-style flow on the same shard: the reduce runs per bucket (a
     25 MB bucket of the whole model's bf16 gradient is 25e6 / (2 W) of this
@@ -391,6 +595,7 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
         # addresses prepared once, so the timed loop is one C call per bucket
         calls.append([([g.data_ptr() + 2 * (c.begin + lo) for g in c.grads], lo, hi,
                        c.parts.data_ptr() + 8 * (nb - 1 - i)) for i, (lo, hi) in enumerate(ranges)])
+
     def event():
         e = torch.cuda.Event(enable_timing=True)
         e.record()   # torch creates the event at its first record
@@ -407,7 +612,8 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
             z.mta_reduce_range(gp, c.plan, lo, hi, part, flags=z.STORE_G, ws=c.ws, stream=stream)
             ev[2 * i + 1].record()
         z.partials_sum(c.parts, nb, c.rsd[rank:rank + 1], stream=stream)
-        z.mta_update(c.grads, c.begin, c.plan, hp(cfg, k + 1), c.rsd, W, flags=z.STORE_G, ws=c.ws, stream=stream)
+        z.mta_update(c.grads, c.begin, c.plan, cfg.hparams(k + 1), c.rsd, W, flags=z.STORE_G, ws=c.ws,
+                     stream=stream)
         ev[2 * nb].record()
         torch.cuda.synchronize()
         red_ms.append(sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(nb)))
@@ -416,30 +622,87 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
                 after_backward_ms=sum(crit_ms) / steps)
 
 
+# ---------------------------------------------------------------------- calibrate mode
+def calibrate(torch, dev, gib=4, spacing_gib=40):
+    """Plain read, write and copy rates of the calibration kernel (the step
+    kernels' access pattern, nothing computed) over `gib` GiB per fp32
+    stream, in two layouts: packed (one torch allocation per buffer) and
+    spaced (buffers spacing_gib GiB apart inside one allocation, like
+    zero1_arena_plan's spaced arrays); plus two mixes shaped like the step's
+    kernels: the store-g update (g, master, m, v read; master, m, v written in
+    place; bf16 parameters written) and the 8-slice reduce (8 bf16 slices
+    read, fp32 g written; spaced: g in the first slot, the slices packed from
+    the fifth, as the arena places them).  Returns a dict of GB/s."""
+    n = (gib << 30) // 4 // 2048 * 2048          # elements per buffer
+    n_tiles = n // 2048
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid, split = 8 * cus, 8
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    # name: (buffers as (bytes per element, spaced slot or None = packed after
+    # the previous buffer), reads as (buffer, bytes), writes likewise)
+    shapes = {
+        "read": ([(4, 0)], [(0, 4)], []),
+        "write": ([(4, 0)], [], [(0, 4)]),
+        "copy": ([(4, 0), (4, 1)], [(0, 4)], [(1, 4)]),
+        "update_mix": ([(4, 0), (4, 1), (4, 2), (4, 3), (2, 4)],
+                       [(0, 4), (1, 4), (2, 4), (3, 4)], [(1, 4), (2, 4), (3, 4), (4, 2)]),
+        "reduce8_mix": ([(4, 0)] + [(2, 4)] + [(2, None)] * 7,
+                        [(k, 2) for k in range(1, 9)], [(0, 4)]),
+    }
+    out = {"elements_per_buffer": n, "workgroups": grid}
+    unit = 2 << 20
+    for layout in ("packed", "spaced"):
+        for name, (bufspec, rspec, wspec) in shapes.items():
+            sizes = [n * b for b, _ in bufspec]
+            if layout == "packed":
+                bufs = [torch.empty(sz, dtype=torch.uint8, device=dev) for sz in sizes]
+                addrs = [t.data_ptr() for t in bufs]
+            else:
+                offs, pos = [], 0
+                for sz, (_, slot) in zip(sizes, bufspec):
+                    o = slot * (spacing_gib << 30) if slot is not None else (pos + unit - 1) // unit * unit
+                    offs.append(o)
+                    pos = o + sz
+                arena = torch.empty(max(o + sz for o, sz in zip(offs, sizes)), dtype=torch.uint8, device=dev)
+                addrs = [arena.data_ptr() + o for o in offs]
+                bufs = [arena]
+            for t in bufs:
+                t.fill_(0x3c)
+            rd = [(addrs[i], b) for i, b in rspec]
+            wr = [(addrs[i], b) for i, b in wspec]
+            fn = lambda: zcal_stream(rd, wr, n_tiles, grid, split, sink.data_ptr(), stream)  # noqa: E731
+            fn()
+            torch.cuda.synchronize()
+            ms = timed_passes(torch, fn, 7)
+            nbytes = n_tiles * 2048 * (sum(b for _, b in rspec) + sum(b for _, b in wspec))
+            out[f"{layout}_{name}_GBps"] = nbytes / (ms * 1e-3) / 1e9
+            log(f"calibrate {layout} {name}: {out[f'{layout}_{name}_GBps']:.0f} GB/s")
+            del bufs, rd, wr, fn
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="C2")
-    ap.add_argument("--design", choices=["auto", "onchip", "store", "recompute"], default="auto")
-    ap.add_argument("--rotate", type=int, default=0, help="independent copies to rotate (0: auto)")
-    ap.add_argument("--layout", choices=["arena", "packed"], default="arena",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--layout", choices=["arena", "packed", "both"], default="both",
                     help="arena: arrays placed by zero1_arena_plan; packed: one torch allocation each")
-    ap.add_argument("--arena-size", choices=["fit", "all"], default="fit",
-                    help="fit: the arena is as large as the plan; all: all free memory less 8 GB")
-    ap.add_argument("--arena-offset-gib", type=float, default=0.0,
-                    help="place the planned layout this far into the arena (tuning; needs --arena-size all)")
+    ap.add_argument("--no-per-config", action="store_true", help="the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--pmc-run", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
-    ap.add_argument("--pmc-also", action="append", default=[], metavar="KERNEL",
-                    help="with --summarize-pmc: also summarize kernels whose name contains this")
     ap.add_argument("--summarize-kt", nargs=2, metavar=("KT_DIR", "OUT"))
     a = ap.parse_args()
 
     if a.summarize_pmc:
-        summarize_pmc(*a.summarize_pmc, also=a.pmc_also)
+        summarize_pmc(*a.summarize_pmc)
         return 0
     if a.summarize_kt:
         summarize_kt(*a.summarize_kt)
@@ -456,26 +719,19 @@ def main():
     import zero_sharded_mixed_zero1_amd as z
     from synth.workloads import configs
 
-    cfg = configs()[a.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    flags = {"auto": 0, "onchip": z.ONCHIP, "store": z.STORE_G, "recompute": z.RECOMPUTE_G}[a.design]
-    store_g = bool(flags & z.STORE_G) or (not (flags & (z.RECOMPUTE_G | z.ONCHIP)) and cfg.W > 4)
-    per_copy = cfg.S * (2 * cfg.W + 26 + (4 if store_g else 0))
-    n_copies = a.rotate or (2 if per_copy < (1 << 30) else 1)
-    st = setup(torch, cfg, flags, n_copies, dev, a.layout, a.arena_size == "all",
-               int(a.arena_offset_gib * (1 << 30)))
-    S, W = st["S"], st["W"]
-    c0 = st["copies"][0]
-    design = z.mta_design(c0.grads, c0.begin, c0.plan, flags)
-    if design == 0:
-        print(f"design {a.design} is not possible for {a.config}", file=sys.stderr)
-        return 2
-    flags = (flags & ~(z.ONCHIP | z.STORE_G | z.RECOMPUTE_G)) | design   # run the resolved design explicitly
-    design_name = {z.ONCHIP: "onchip", z.STORE_G: "store_g", z.RECOMPUTE_G: "recompute_g"}[design]
+    if a.calibrate:
+        out = {"calibrate": calibrate(torch, dev), "device": torch.cuda.get_device_properties(dev).name}
+        print(json.dumps(out), flush=True)
+        return 0
 
+    cfgs = configs()
+    cfg = cfgs[a.config]
     if a.pmc_run:
-        run_steps(z, cfg, st, flags, 0, 4)
+        st = setup(torch, cfg, z.STORE_G if cfg.W > 4 else z.RECOMPUTE_G, 1, dev,
+                   "packed" if a.layout == "packed" else "arena")
+        run_steps(z, cfg, st, z.STORE_G if cfg.W > 4 else z.RECOMPUTE_G, 0, 4)
         x = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         y = torch.empty_like(x)
         torch.cuda.synchronize()
@@ -485,92 +741,77 @@ def main():
         print("pmc run done", flush=True)
         return 0
 
-    run_steps(z, cfg, st, flags, 0, a.warmup)
-    torch.cuda.synchronize()
-    # the timed region: exactly K steps back to back, bracketed by synchronizations
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g0.record()
-    run_steps(z, cfg, st, flags, a.warmup, a.warmup + a.steps)
-    g1.record()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    gpu_ms_per_step = g0.elapsed_time(g1) / a.steps
-    # each kernel's own duration: the same K steps again, the reduce and the
-    # update of each stamped by their own dispatches (HIP events; the single
-    # launch is bracketed by stream markers on the stream it runs on)
-    def event():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()   # torch creates the event at its first record
-        return e
+    layouts = ["arena", "packed"] if a.layout == "both" else [a.layout]
 
-    events = [((event(), event()), (event(), event())) for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    run_steps(z, cfg, st, flags, a.warmup + a.steps, a.warmup + 2 * a.steps, events)
-    torch.cuda.synchronize()
-    two_phase = bool(flags & (z.STORE_G | z.RECOMPUTE_G))
-    kern_ms = [e[1 if two_phase else 0][0].elapsed_time(e[1 if two_phase else 0][1]) for e in events]
-    red_ms = [e[0][0].elapsed_time(e[0][1]) for e in events] if two_phase else None
-    ms_per_step = el * 1e3 / a.steps
-    value = S / (ms_per_step * 1e-3)
-    bpp = cfg.bytes_per_param
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    # algorithmic bytes per launch of the dominant kernel: the whole step
-    # (2W+26 B/param) for the single launch; master/m/v read+write and the
-    # bf16 write (26 B/param, 18 with bf16 m,v) for the two-phase update
-    kern_bytes = ((18 if cfg.mv_bf16 else 26) if two_phase else bpp) * S
-    kern_name = UPDATE_KERNEL if two_phase else ONCHIP_KERNEL
-    achieved = kern_bytes / (kern_avg * 1e-3) / 1e9
-    traffic = traffic_from_summary(PMC_SUMMARY, kern_name) if (a.config == "C2" and a.design == "auto") else None
+    def steps_for(name):
+        return max(a.steps, MIN_STEPS.get(name, 0))
+
+    # the headline workload: exactly --steps timed steps after --warmup, per layout
+    head = {}
+    for lay in layouts:
+        log(f"{cfg.name} {lay}: setup + {a.warmup} warmup + {a.steps} timed steps")
+        head[lay] = measure(torch, z, cfg, lay, a.steps, a.warmup, dev, bucketed=(cfg.name == "C2"))
+        log(f"{cfg.name} {lay}: {head[lay]['ms_per_step']:.4f} ms/step, "
+            f"{head[lay]['pct_of_peak_hbm']:.1f}% of 8 TB/s")
+    main_lay = layouts[0]
+    h = head[main_lay]
+    S, W = cfg.S, cfg.W
+    upd = h["kernels"]["update"]
     out = {
         "metric": "params updated/s and achieved HBM GB/s (% of peak) per fused ZeRO-1 step",
-        "value": value,
+        "value": h["params_per_s"],
         "unit": "params/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded SplitMix64 Irwin-Hall gradients and masters; tensor shapes only, no weights)",
         "config": {
-            "workload": cfg.workload,
-            "W": W, "rank": st["rank"], "shard_params": S, "pieces": st["pieces"],
-            "bytes_per_param": bpp, "design": design_name,
-            "rotated_copies": n_copies, "m_v": "bf16" if cfg.mv_bf16 else "fp32",
-            "memory_layout": st["info"],
+            "workload": cfg.workload, "W": W, "rank": cfg.rank, "shard_params": S,
+            "bytes_per_param": cfg.bytes_per_param, "design": "store_g" if W > 4 else "recompute_g",
+            "m_v": "bf16" if cfg.mv_bf16 else "fp32", "memory_layout": h["layout"],
         },
-        "algorithmic_GBps": value * bpp / 1e9,
-        "pct_of_peak_hbm": 100.0 * value * bpp / 1e9 / PEAK_HBM_GBS,
-        "gpu_ms_per_step": gpu_ms_per_step,
-        "kernel_ms": kern_avg,
-        "reduce_kernel_ms": sum(red_ms) / len(red_ms) if red_ms else None,
-        "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": kern_bytes},
+        "algorithmic_GBps": h["algorithmic_GBps"],
+        "pct_of_peak_hbm": h["pct_of_peak_hbm"],
+        "gpu_ms_per_step": h["gpu_ms_per_step"],
+        "roofline": {"bound": "hbm", "kernel": UPDATE_KERNEL, "achieved": upd["algorithmic_GBps"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": upd["algorithmic_GBps"] / PEAK_HBM_GBS,
+                     "traffic": upd["traffic"], "algorithmic_bytes_per_launch": upd["algorithmic_bytes"],
+                     "kernel_ms": upd["ms"], "ceiling_ms": upd.get("ceiling_ms"),
+                     "frac_of_ceiling": upd.get("frac_of_ceiling")},
+        "kernels": h["kernels"],
+        "ceiling_ms_per_step": h.get("ceiling_ms_per_step"),
+        "layouts": {lay: {k: head[lay][k] for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout")}
+                    for lay in layouts},
     }
-    if red_ms:
-        # both kernels of the two-phase step: bytes the step's algorithm needs
-        # and bytes the design moves (+ the fp32 g written and re-read, or the
-        # slices re-read), over each kernel's own time
-        red_avg = sum(red_ms) / len(red_ms)
-        store_g = bool(flags & z.STORE_G)
-        red_alg, red_mv = 2 * W * S, (2 * W + (4 if store_g else 0)) * S
-        upd_mv = kern_bytes + (4 if store_g else 2 * W) * S
-        out["kernels"] = {
-            "reduce": {"ms": red_avg, "algorithmic_bytes": red_alg, "moved_bytes": red_mv,
-                       "algorithmic_GBps": red_alg / (red_avg * 1e-3) / 1e9,
-                       "moved_GBps": red_mv / (red_avg * 1e-3) / 1e9},
-            "update": {"ms": kern_avg, "algorithmic_bytes": kern_bytes, "moved_bytes": upd_mv,
-                       "algorithmic_GBps": achieved, "moved_GBps": upd_mv / (kern_avg * 1e-3) / 1e9},
-        }
-    if flags & z.STORE_G:
-        out["bucketed"] = bucketed_timing(torch, z, cfg, st, a.warmup + 2 * a.steps, min(a.steps, 50))
+    if "bucketed" in h:
+        out["bucketed"] = h["bucketed"]
+    if not a.no_per_config:
+        per = {}
+        for name in PER_CONFIG:
+            if name == cfg.name:
+                continue
+            c = cfgs[name]
+            per[name] = {"workload": c.workload, "W": c.W, "shard_params": c.S, "bytes_per_param": c.bytes_per_param,
+                         "design": "store_g" if c.W > 4 else "recompute_g"}
+            for lay in layouts:
+                k = steps_for(name)
+                log(f"{name} {lay}: setup + {a.warmup} warmup + {k} timed steps")
+                r = measure(torch, z, c, lay, k, a.warmup, dev, bucketed=(name == "C2"))
+                log(f"{name} {lay}: {r['ms_per_step']:.4f} ms/step, {r['pct_of_peak_hbm']:.1f}% of 8 TB/s")
+                per[name][lay] = r
+        out["per_config"] = per
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, S, st["begin"])
+        log("cpu baseline (oracle, 1 thread and N threads)")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+        if not a.no_per_config:
+            for name in PER_CONFIG:
+                if name in out.get("per_config", {}):
+                    out["per_config"][name]["cpu_baseline"] = cpu_baseline(cfgs[name])
     print(json.dumps(out), flush=True)
     return 0
 

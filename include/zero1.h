@@ -36,8 +36,8 @@
  *     surfaces at the caller's next synchronization.  Setting the environment
  *     variable ZERO1_SYNC_CHECK=1 makes each call synchronize and check (tests;
  *     on a stream under graph capture it checks the launches only).
- *   - Graph capture: apart from zero1_mta_plan (a synchronous table upload) and
- *     the ZERO1_ONCHIP cooperative launch, the entry points only launch kernels
+ *   - Graph capture: apart from zero1_mta_plan (a synchronous table upload),
+ *     the entry points only launch kernels
  *     (no memset, copy or synchronization), so their work can be captured into
  *     a HIP graph.  The fp32 scalars derived from zero1_hparams -- the step t
  *     included -- are kernel arguments and are frozen into the graph, unless
@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ZERO1_ABI_VERSION 3
+#define ZERO1_ABI_VERSION 4
 #define ZERO1_MAX_W 128          /* largest number of replicas per call */
 
 typedef enum zero1_status {
@@ -87,15 +87,10 @@ typedef enum zero1_status {
 #define ZERO1_MV_BF16      0x2u  /* m and v are stored as bf16 (uint16_t)           */
 #define ZERO1_RECOMPUTE_G  0x4u  /* step: the update re-reads the W slices          */
 #define ZERO1_STORE_G      0x8u  /* step: the reduce stores fp32 g in the workspace
-                                    and the update reads it back                     */
-#define ZERO1_ONCHIP       0x10u /* zero1_mta_step only: one cooperative launch that
-                                    keeps g in registers across a grid barrier
-                                    (exactly 2W+26 bytes/param); EINVAL when the
-                                    shard does not fit in one co-resident grid.
-                                    Opt-in: on MI355X the cooperative launch and the
-                                    grid barrier cost more than the g round trip
-                                    they save.  No design flag: STORE_G when W > 4
-                                    (fewer bytes than re-reading), else RECOMPUTE_G. */
+                                    and the update reads it back.  Neither design
+                                    flag: STORE_G when W > 4 (fewer bytes than
+                                    re-reading the slices), else RECOMPUTE_G.     */
+/* 0x10u is unused (rejected as an unknown flag). */
 
 /* Compatibility variants (not the pages' step; off by default):
  *   ZERO1_DECAY_FIRST  decay the master before the Adam update, the order
@@ -284,10 +279,9 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads,
  *   step needs from other ranks once the gradients are reduced).
  * zero1_mta_step: the whole step (1-5) for rank my_rank when the other
  *   ranks' partials are already in rank_sumsq; entry my_rank is overwritten
- *   with this rank's partial.  Either one cooperative launch (ZERO1_ONCHIP,
- *   on request) or zero1_mta_reduce with sumsq_out = rank_sumsq + my_rank
- *   followed by zero1_mta_update.
- *   flags: one of ZERO1_ONCHIP / ZERO1_STORE_G / ZERO1_RECOMPUTE_G (none:
+ *   with this rank's partial: zero1_mta_reduce with sumsq_out =
+ *   rank_sumsq + my_rank followed by zero1_mta_update.
+ *   flags: ZERO1_STORE_G or ZERO1_RECOMPUTE_G (neither:
  *   the library picks, see zero1_mta_design), ZERO1_SUM_ONLY and the
  *   compatibility variants ZERO1_DECAY_FIRST, ZERO1_CLIP_EPS, ZERO1_G_BF16
  *   (ZERO1_MV_BF16 comes from the plan).
@@ -325,7 +319,7 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
  *   is replica w's gradient of shard element lo + k (bf16, device); g for the
  *   range is stored in the workspace (sized by zero1_mta_workspace_bytes(plan,
  *   W, ZERO1_STORE_G)) and the range's fp64 sum of squares goes to *sumsq_out.
- *   flags: ZERO1_SUM_ONLY, ZERO1_G_BF16 (RECOMPUTE_G / ONCHIP: EINVAL).
+ *   flags: ZERO1_SUM_ONLY, ZERO1_G_BF16 (RECOMPUTE_G: EINVAL).
  * zero1_partials_sum: *sum_out = parts[0] + parts[1] + ... (n <= 8192 doubles,
  *   device), added in a fixed order (deterministic). */
 zero1_status zero1_mta_reduce_range(const uint16_t* const* grads, int W,
@@ -336,8 +330,8 @@ zero1_status zero1_partials_sum(const double* parts, int n, double* sum_out,
                                 void* stream);
 
 /* Which design zero1_mta_step would run for these arguments on the current
- * device: ZERO1_ONCHIP, ZERO1_STORE_G or ZERO1_RECOMPUTE_G; 0 when the
- * arguments are invalid or an explicitly requested design is impossible. */
+ * device: ZERO1_STORE_G or ZERO1_RECOMPUTE_G; 0 when the arguments are
+ * invalid or both design flags are given. */
 int zero1_mta_design(const uint16_t* const* grads, int W, int64_t begin,
                      const zero1_plan* plan, uint32_t flags);
 zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
@@ -365,8 +359,7 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
  * The events are created and owned by the caller (hipEventCreate, timing
  * enabled, on the device the step runs on) and must outlive the kernel.
  * Errors surface in the step call: ZERO1_EHIP when its stream is being
- * captured into a graph (kernel-scoped events cannot be captured), ZERO1_EINVAL
- * for the single cooperative launch (ZERO1_ONCHIP), which takes no events.
+ * captured into a graph (kernel-scoped events cannot be captured).
  * Host only; always ZERO1_OK. */
 zero1_status zero1_time_next_launch(void* start_event, void* stop_event);
 
@@ -381,8 +374,9 @@ zero1_status zero1_time_next_launch(void* start_event, void* stop_event);
  * W-slice reduce is faster when the slices sit well away from g (7.5e9/64
  * shard: 2.40 vs 2.90 ms).  The planner puts those five at one spacing D
  * (40 GiB, or more when an array is larger, or less when `capacity` is short)
- * and packs the remaining gradient buffers after the parameter buffer.  The gaps between the spaced arrays are
- * not used by the library: the caller may place its other tensors there.
+ * and packs the remaining gradient buffers after the parameter buffer.  The
+ * gaps between the spaced arrays are not used by the library: the caller may
+ * place its other tensors there.
  *
  * Request: shard_len S >= 1; W in 1..ZERO1_MAX_W gradient buffers of
  * grad_elems bf16 each, this rank's shard starting at element grad_offset of
@@ -390,8 +384,8 @@ zero1_status zero1_time_next_launch(void* start_event, void* stop_event);
  * the shard's begin and N for full replicas); the flat bf16 parameter buffer
  * of param_elems elements with the shard starting at param_offset; flags:
  * ZERO1_MV_BF16 (2-byte m, v) and the design (ZERO1_STORE_G, ZERO1_RECOMPUTE_G,
- * or neither for the one zero1_mta_step picks; ZERO1_ONCHIP is planned like
- * RECOMPUTE_G); capacity: the largest arena the caller can allocate.
+ * or neither for the one zero1_mta_step picks); capacity: the largest arena
+ * the caller can allocate.
  *
  * Layout (byte offsets from the arena base, which must be 2 MiB aligned): the
  * workspace (ws_bytes = zero1_mta_workspace_bytes for that design; holds g),

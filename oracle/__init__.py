@@ -93,6 +93,8 @@ def lib():
         L.oracle_round_to_bf16.restype = None
         L.oracle_zero_bytes_per_gpu.argtypes = [f64, f64, f64, i32]
         L.oracle_zero_bytes_per_gpu.restype = f64
+        L.oracle_threads.argtypes = [i32]
+        L.oracle_threads.restype = i32
         _lib = L
     return _lib
 
@@ -244,3 +246,9 @@ def step(grads, master, m, v, param_bf16, hp, rank_sumsq, my_rank, average=True,
 
 def zero_bytes_per_gpu(psi, K, n_d, stage) -> float:
     return float(lib().oracle_zero_bytes_per_gpu(float(psi), float(K), float(n_d), int(stage)))
+
+
+def threads(n: int = 0) -> int:
+    """Set the OpenMP thread count of the oracle's loops (n > 0) and return
+    the count in effect (oracle_threads; no arithmetic)."""
+    return int(lib().oracle_threads(int(n)))

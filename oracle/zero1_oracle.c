@@ -29,6 +29,7 @@
  * order of magnitude is pinned, under a stated reading of both).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 #include <xmmintrin.h>
@@ -251,18 +252,19 @@ void oracle_adamw_scalars(double lr, double beta1, double beta2, double eps,
 /* ---------------------------------------------------------------------- */
 
 /*
- * One element of the page's AdamW, in its order ([PT] mixed precision +
- * AdamW code):
- *   m <- beta1*m + (1-beta1)*g
- *   v <- beta2*v + (1-beta2)*(g*g)
- *   p <- p - step_size * m / (sqrt(v) + eps)
- *   p <- p * (1 - lr*weight_decay)        (update first, then decay)
- * and the bf16 parameter the forward pass reads is the nearest bf16 of the
- * new master ([PT]: the fp32 master receives the update and a bf16 copy is
- * made every step).  g is the (possibly clipped) reduced gradient.
- * decay_first = 1 swaps the last two lines (decay, then update): the order
- * the page attributes to torch.optim.AdamW, which it says differs by a term
- * of order lr^2 * lambda per step.
+ * One element of AdamW with decoupled weight decay, as [PT] "一张卡上装了什么：
+ * 混合精度与 AdamW" defines it, in this file's notation (g already clipped,
+ * sigma_t and delta from oracle_adamw_scalars):
+ *   m_t = b1 m_{t-1} + a1 g                 (first moment, a1 = 1 - beta1)
+ *   v_t = b2 v_{t-1} + a2 (g g)             (second moment, a2 = 1 - beta2)
+ *   p_t = (p_{t-1} - sigma_t m_t / (sqrt(v_t) + eps)) delta
+ * The decay factor delta multiplies the master after the Adam move (the
+ * section's order); each operation is one binary32 operation, evaluated left
+ * to right as written.  decay_first = 1 applies delta before the move
+ * instead: the order the section attributes to torch.optim.AdamW, which it
+ * says differs by a term of order lr^2 * lambda per step.  The bf16 parameter
+ * of the forward pass is then the nearest bf16 of p_t (same section: the fp32
+ * master takes the update, a bf16 copy is made every step).
  */
 static void adamw_one(float g, float* p, float* m, float* v,
                       const oracle_scalars* s, int decay_first)
@@ -440,4 +442,16 @@ double oracle_zero_bytes_per_gpu(double psi, double K, double n_d, int stage)
     case 3: return (2.0 + 2.0 + K) * psi / n_d;
     default: return -1.0;
     }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Harness helper (no arithmetic)                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Sets the number of OpenMP threads the loops above use when n > 0 and
+ * returns the number in effect (the CPU baseline times 1 and N threads). */
+int oracle_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
 }

@@ -76,7 +76,7 @@ static void arena_case(int64_t S, int W, int64_t ge, int64_t go, int64_t pe, int
 int main(void)
 {
     /* ------------------------------------------------------------ arena */
-    const uint32_t designs[] = {0, ZERO1_STORE_G, ZERO1_RECOMPUTE_G, ZERO1_ONCHIP, ZERO1_MV_BF16,
+    const uint32_t designs[] = {0, ZERO1_STORE_G, ZERO1_RECOMPUTE_G, ZERO1_RECOMPUTE_G | ZERO1_MV_BF16, ZERO1_MV_BF16,
                                 ZERO1_STORE_G | ZERO1_MV_BF16};
     const int Ws[] = {1, 2, 4, 8, 64, 127, 128};
     const int64_t Ss[] = {1, 4097, 15554976, 117187500};

@@ -182,6 +182,10 @@ def test_unknown_flags_are_rejected():
     bufs = [FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20)]
     assert "unknown flag" in _einval(lambda: z.adamw_step(FAKE + (4 << 20), None, 0, 100, *bufs, _hp(),
                                                           FAKE + (5 << 20), 1, flags=0x100, stream=0))
+    # 0x10 belonged to a single-launch design that is no longer in the library
+    plan = z.Plan(table=FAKE, shard_len=1000, n_pieces=1, n_chunks=1, chunk_elems=2048)
+    assert "unknown flag" in _einval(lambda: z.mta_step(g, 0, plan, _hp(), FAKE, 2, 0, flags=0x10,
+                                                        ws=FAKE, ws_bytes=1 << 30, stream=0))
 
 
 def test_bucketed_reduction_rejects_bad_arguments():
@@ -325,8 +329,8 @@ def test_bench_entry_points_and_gpu_count_contract():
     import subprocess
     import sys
     import bench
-    for name in ("setup", "run_steps", "cpu_baseline", "bucketed_timing", "summarize_pmc", "summarize_kt",
-                 "traffic_from_summary", "kernel_source_hash", "main"):
+    for name in ("setup", "run_steps", "measure", "ceilings", "calibrate", "cpu_baseline", "bucketed_timing",
+                 "summarize_pmc", "summarize_kt", "traffic_from_summary", "kernel_source_hash", "main"):
         assert callable(getattr(bench, name)), name
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
@@ -356,15 +360,16 @@ def test_profile_summaries_from_counter_and_trace_files(tmp_path):
                 rows.append(f'{disp},"{names[key]}",C,{v / 2}')
         (d / "x" / "pmc_counter_collection.csv").write_text("\n".join(rows) + "\n")
     out = tmp_path / "summary.txt"
-    bench.summarize_pmc(str(fetch), str(write), str(out), also=["reduce_kernel<true, true, true, false, 0>"])
+    bench.summarize_pmc(str(fetch), str(write), str(out))
     kv = dict(l.split(" = ", 1) for l in out.read_text().splitlines() if " = " in l and not l.startswith("#"))
     # fetch scale: 1 GiB / (524288 KiB) = x2; write scale x1; medians 101 / 70 and 40 / 11 KiB
-    assert int(kv["dominant_fetch_bytes"]) == 101 * 1024 * 2 and int(kv["dominant_write_bytes"]) == 70 * 1024
-    assert int(kv["also_fetch_bytes"]) == 40 * 1024 * 2 and int(kv["also_write_bytes"]) == 11 * 1024
-    assert bench.traffic_from_summary(str(out), bench.UPDATE_KERNEL) == 101 * 2048 + 70 * 1024
+    assert int(kv["update_fetch_bytes"]) == 101 * 1024 * 2 and int(kv["update_write_bytes"]) == 70 * 1024
+    assert int(kv["reduce_fetch_bytes"]) == 40 * 1024 * 2 and int(kv["reduce_write_bytes"]) == 11 * 1024
+    assert bench.traffic_from_summary(str(out), "update") == 101 * 2048 + 70 * 1024
+    assert bench.traffic_from_summary(str(out), "reduce") == 40 * 2048 + 11 * 1024
     stale = tmp_path / "stale.txt"
     stale.write_text(out.read_text().replace(bench.kernel_source_hash(), "0" * 16))
-    assert bench.traffic_from_summary(str(stale), bench.UPDATE_KERNEL) is None
+    assert bench.traffic_from_summary(str(stale), "update") is None
     # kernel trace: two grids of one kernel are reported apart
     kt = tmp_path / "kt" / "x"
     kt.mkdir(parents=True)

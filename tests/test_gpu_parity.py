@@ -191,14 +191,10 @@ def test_adamw_step_flat_parity(env, mv_bf16, source):
 # ---------------------------------------------------------------- multi-tensor apply
 RAGGED = [3000, 17, 5000, 8, 2203, 1, 65536 + 3, 768, 8192 * 2, 40000]
 # ragged against the 2048-element tiles but every piece 8-aligned, and a total
-# that every W in the tests cuts into 8-aligned shards: what the single-launch
-# (on-chip) design needs, and what real tensor lists look like
+# that every W in the tests cuts into 8-aligned shards (what real tensor lists
+# look like: the vector path end to end)
 RAGGED8 = [3000, 16, 5000, 8, 2208, 8, 65536 + 8, 768, 8192 * 2, 40120]
 assert sum(RAGGED8) % (8 * 24) == 0
-
-
-def ragged_for(design):
-    return RAGGED8 if design == z.ONCHIP else RAGGED
 
 
 VARIANT_FLAGS = {oracle.DECAY_FIRST: z.DECAY_FIRST, oracle.CLIP_EPS: z.CLIP_EPS, oracle.G_BF16: z.G_BF16}
@@ -268,29 +264,29 @@ def run_mta_all_ranks(torch, dev, numels, W, steps, seed, flags, mv_bf16, flat_s
 
 
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_mta_parity_ragged_all_ranks(env, W, design):
     torch, dev = env
-    run_mta_all_ranks(torch, dev, ragged_for(design), W, 3, 0xA000 + W, design, False, True,
+    run_mta_all_ranks(torch, dev, RAGGED, W, 3, 0xA000 + W, design, False, True,
                       lambda t: [0.02, 1e-4, 0.3][t % 3])
 
 
 @pytest.mark.parametrize("mv_bf16,flat_state", [(True, True), (False, False), (True, False)])
 def test_mta_parity_state_layouts(env, mv_bf16, flat_state):
     torch, dev = env
-    for design in (z.ONCHIP, z.STORE_G, z.RECOMPUTE_G):
-        run_mta_all_ranks(torch, dev, ragged_for(design), 4, 3, 0xB000, design, mv_bf16, flat_state,
+    for design in (z.STORE_G, z.RECOMPUTE_G):
+        run_mta_all_ranks(torch, dev, RAGGED, 4, 3, 0xB000, design, mv_bf16, flat_state,
                           lambda t: [0.02, 1e-4, 0.3][t % 3])
 
 
 @pytest.mark.parametrize("W", [3, 8])
-@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_mta_sum_only_parity(env, W, design):
     """ZERO1_SUM_ONLY (the reduce keeps the sum, no average) through the whole
     multi-tensor step on every design, every rank, against the oracle's
     unaveraged step."""
     torch, dev = env
-    run_mta_all_ranks(torch, dev, ragged_for(design), W, 2, 0xD800 + W, design, False, True,
+    run_mta_all_ranks(torch, dev, RAGGED, W, 2, 0xD800 + W, design, False, True,
                       lambda t: 0.05, sum_only=True)
 
 
@@ -313,24 +309,24 @@ DEGENERATE_HP = {
 
 
 @pytest.mark.parametrize("name", list(DEGENERATE_HP))
-@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_degenerate_hyperparameters(env, name, design):
     """Every design on a ragged list, three steps, one rank (fp32 moments) and
     another (bf16 moments), bit-exact against the oracle."""
     torch, dev = env
     kw = DEGENERATE_HP[name]
     for r, mv_bf16 in ((1, False), (2, True)):
-        run_mta_all_ranks(torch, dev, ragged_for(design), 3, 3, 0xDE00 + r, design, mv_bf16, True,
+        run_mta_all_ranks(torch, dev, RAGGED, 3, 3, 0xDE00 + r, design, mv_bf16, True,
                           lambda t: [0.02, 1e-4, 0.3][t % 3], ranks=[r], hp_kw=kw)
 
 
 @pytest.mark.parametrize("variant", [oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
                                      oracle.DECAY_FIRST | oracle.CLIP_EPS | oracle.G_BF16])
-@pytest.mark.parametrize("design", [z.ONCHIP, z.STORE_G, z.RECOMPUTE_G])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_compat_variants_parity(env, variant, design):
     """Decay-first order, the torch clip convention and a bf16 reduced
     gradient (with bf16 moments), each against the oracle's variant, every
-    rank, 3 steps, all three step designs."""
+    rank, 3 steps, both step designs."""
     torch, dev = env
     run_mta_all_ranks(torch, dev, RAGGED8, 4, 3, 0xD000 + variant, design, variant == oracle.G_BF16, True,
                       lambda t: [0.02, 1e-4, 0.3][t % 3], variant=variant)
@@ -407,22 +403,6 @@ def test_c1_full_trajectory(env, design):
                       lambda t: c.sigma)
 
 
-def test_onchip_rejects_what_does_not_fit(env):
-    torch, dev = env
-    master_full = synth.f32(20000, 1, 0, 0.02)
-    a = MtaShard(torch, dev, [13, 19987], 1, 0, master_full)      # misaligned second piece
-    ws = a.workspace(z.ONCHIP)
-    gd = [torch.zeros(20000, dtype=torch.int16, device=dev)]
-    rs = torch.zeros(1, dtype=torch.float64, device=dev)
-    with pytest.raises(z.Zero1Error) as e:
-        z.mta_step(gd, 0, a.plan, hp_at(1), rs, 1, 0, flags=z.ONCHIP, ws=ws)
-    assert "ONCHIP" in e.value.message
-    with pytest.raises(z.Zero1Error):
-        z.mta_reduce(gd, 0, a.plan, rs, flags=z.ONCHIP, ws=ws)
-    with pytest.raises(z.Zero1Error):
-        z.mta_step(gd, 0, a.plan, hp_at(1), rs, 1, 0, flags=z.ONCHIP | z.STORE_G, ws=ws)
-
-
 # ---------------------------------------------------------------- properties
 def test_mta_equals_reduce_plus_adamw(env):
     torch, dev = env
@@ -453,32 +433,6 @@ def test_mta_equals_reduce_plus_adamw(env):
     assert_f32_equal(m, fmm.cpu().numpy(), "m")
     assert_f32_equal(v, fvv.cpu().numpy(), "v")
     assert_bf16_equal(param, to_np_u16(fp), "param")
-
-
-def test_onchip_equals_two_phase(env):
-    """The single-launch step and the two-kernel step give the same state bit
-    for bit (their fp64 partials may differ in the last bits only)."""
-    torch, dev = env
-    W, r = 8, 3
-    N = 8 * 23456            # 8-aligned shards; each ends in a partial 2048-element tile
-    master_full = synth.f32(N, synth.master_key(12), 0, 0.02)
-    a = MtaShard(torch, dev, [N], W, r, master_full)
-    b = MtaShard(torch, dev, [N], W, r, master_full)
-    wa, wb = a.workspace(z.ONCHIP), b.workspace(z.STORE_G)
-    for t in range(1, 5):
-        G = replicas(12, t, W, N, 0.3)
-        gd = [to_dev_u16(torch, x, dev) for x in G]
-        ra = torch.full((W,), 0.25, dtype=torch.float64, device=dev)
-        rb = ra.clone()
-        ia = torch.zeros(4, dtype=torch.float64, device=dev)
-        ib = torch.zeros(4, dtype=torch.float64, device=dev)
-        z.mta_step(gd, a.begin, a.plan, hp_at(t), ra, W, r, flags=z.ONCHIP, info_out=ia, ws=wa)
-        z.mta_step(gd, b.begin, b.plan, hp_at(t), rb, W, r, flags=z.STORE_G, info_out=ib, ws=wb)
-        torch.cuda.synchronize()
-        assert rel_close(ra[r].item(), rb[r].item(), NORM_TOL)
-        assert ia.cpu().numpy()[2:4].tobytes() == ib.cpu().numpy()[2:4].tobytes()   # coef, clip, flags
-    for x, y in zip(a.gather(), b.gather()):
-        assert x.tobytes() == y.tobytes()
 
 
 def test_rerun_is_bit_identical_and_resume_is_exact(env):
@@ -780,13 +734,12 @@ def test_mta_step_captured_in_a_graph(env, design):
     del graph
 
 
-@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G, z.ONCHIP])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_device_scalars_replay_changes_step_and_lr(env, design):
     """One step captured with its hyper-parameters in device memory, replayed
     for t = 1..4 under a changing learning rate (the scalars of each step
     derived on the host and copied in before its replay), equals four eager
-    calls with host hyper-parameters and the oracle's four steps.  ONCHIP is
-    run eagerly with device scalars (its cooperative launch is not captured)."""
+    calls with host hyper-parameters and the oracle's four steps."""
     torch, dev = env
     numels, W, r = RAGGED8, 4, 3
     N = sum(numels)
@@ -806,22 +759,17 @@ def test_device_scalars_replay_changes_step_and_lr(env, design):
     host_scal = torch.zeros(40, dtype=torch.uint8).pin_memory()
     hp_dev = {"device_scalars": dev_scal}
     step = lambda: z.mta_step(gd, replay.begin, replay.plan, hp_dev, rsd_g, W, r, flags=design, ws=ws_g)
-    graph = None
-    if design != z.ONCHIP:
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
     for t, lr in [(1, 1e-3), (2, 6e-4), (3, 3e-4), (4, 1e-4)]:
         hp = hp_at(t, lr=lr)
         s = z.step_scalars_derive(hp)
         host_scal.copy_(torch.frombuffer(bytearray(bytes(s)), dtype=torch.uint8))
         dev_scal.view(torch.uint8).copy_(host_scal, non_blocking=True)
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
+        graph.replay()
         z.mta_step(gd, eager.begin, eager.plan, hp, rsd_e, W, r, flags=design, ws=ws_e)
         torch.cuda.synchronize()
         oracle.step([g[eager.begin:eager.begin + eager.S] for g in G], o.master, o.m, o.v, o.param, hp,
@@ -967,7 +915,7 @@ def test_two_streams_run_two_ranks_concurrently(env):
         assert_bf16_equal(p, ost[r].param, f"param rank {r}")
 
 
-@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G, z.ONCHIP])
+@pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_zero_gradients(env, design):
     """Degenerate input: every replica's gradient is +0 (step 1) or -0 (step 2),
     then eps = 0 (step 3, 0/0 by IEEE).  Norm 0, no clip, a pure decay of the
@@ -1011,17 +959,17 @@ def test_random_configurations(env, case):
     torch, dev = env
     rng = np.random.default_rng(0xC0FFEE + case)
     W = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
-    onchip = case % 5 == 4
+    aligned = case % 5 == 4
     n_t = int(rng.integers(1, 31))
     kinds = rng.choice(3, size=n_t, p=[0.4, 0.4, 0.2])
     sizes = [int(rng.integers(1, 41)) if k == 0 else int(rng.integers(100, 5001)) if k == 1
              else int(rng.integers(10000, 70001)) for k in kinds]
-    if onchip:   # pieces and shard boundaries on 8-element boundaries
+    if aligned:   # pieces and shard boundaries on 8-element boundaries (the vector path)
         sizes = [8 * max(1, s // 8) for s in sizes]
         S0 = -(-sum(sizes) // W)
         S0 = -(-S0 // 8) * 8
         sizes[-1] += W * S0 - sum(sizes)
-    design = z.ONCHIP if onchip else int(rng.choice([z.STORE_G, z.RECOMPUTE_G]))
+    design = int(rng.choice([z.STORE_G, z.RECOMPUTE_G]))
     mv_bf16 = bool(rng.integers(0, 2))
     flat_state = bool(rng.integers(0, 2))
     variant = int(rng.choice([0, 0, oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
@@ -1096,7 +1044,7 @@ def test_kernel_scoped_timing(env):
     untimed one; each kernel's own duration is positive and the two together
     take less than the same calls bracketed by stream markers; a request is
     dropped when the next step call returns, also when that call fails; a
-    capturing stream and the single cooperative launch refuse it."""
+    capturing stream refuses it."""
     torch, dev = env
     numels, W, r = RAGGED8, 4, 1
     N = sum(numels)
@@ -1147,13 +1095,6 @@ def test_kernel_scoped_timing(env):
     z.mta_reduce(gd, timed.begin, timed.plan, rsd_t[r:r + 1], flags=z.STORE_G, ws=ws_t)
     torch.cuda.synchronize()
     assert a.elapsed_time(b) == before
-
-    # the cooperative single launch takes no events
-    z.time_next_launch(a, b)
-    with pytest.raises(z.Zero1Error) as ei:
-        z.mta_step(gd, timed.begin, timed.plan, hp_at(4), rsd_t, W, r, flags=z.ONCHIP,
-                   ws=timed.workspace(z.ONCHIP))
-    assert ei.value.name == "ZERO1_EINVAL" and "timing" in ei.value.message
 
     # a stream being captured refuses the request before launching; the same
     # call without it is captured and replays like an eager call

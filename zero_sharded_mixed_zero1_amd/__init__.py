@@ -7,7 +7,7 @@ library is missing, importing the binding functions raises.
 """
 from .binding import (  # noqa: F401
     Zero1Error, HParams, NormInfo, Piece, Plan, ArenaRequest, ArenaLayout, StepScalars,
-    SUM_ONLY, MV_BF16, RECOMPUTE_G, STORE_G, ONCHIP, DECAY_FIRST, CLIP_EPS, G_BF16, MAX_W,
+    SUM_ONLY, MV_BF16, RECOMPUTE_G, STORE_G, DECAY_FIRST, CLIP_EPS, G_BF16, MAX_W,
     abi_version, last_error, shard_range, workspace_bytes,
     shard_reduce, grad_norm, adamw_step,
     mta_table_bytes, mta_plan, mta_workspace_bytes, mta_reduce, mta_update, mta_design, mta_step, mta_reduce_range, partials_sum,

@@ -11,21 +11,21 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# ZERO1_LIB points the binding at another build of the same library (tuning)
+# ZERO1_LIB points the binding at another build of the same library (for
+# instance one built with other compile-time launch constants)
 lib_path = os.environ.get("ZERO1_LIB") or os.path.join(HERE, "libzero1.so")
 
 SUM_ONLY = 0x1
 MV_BF16 = 0x2
 RECOMPUTE_G = 0x4
 STORE_G = 0x8
-ONCHIP = 0x10
 DECAY_FIRST = 0x20
 CLIP_EPS = 0x40
 G_BF16 = 0x80
 MAX_W = 128
 # the layout of the structures below and the signatures set in lib(); a
 # library that reports another ZERO1_ABI_VERSION is refused at load time
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 P = ctypes.c_void_p
 i64 = ctypes.c_int64
@@ -320,7 +320,7 @@ def partials_sum(parts, n: int, sum_out, stream=None):
 
 
 def mta_design(grads, begin: int, plan: Plan, flags: int = 0) -> int:
-    """The design flag (ONCHIP, STORE_G or RECOMPUTE_G) mta_step would run; 0 if none."""
+    """The design flag (STORE_G or RECOMPUTE_G) mta_step would run; 0 if none."""
     arr = _ptrs(grads)
     return lib().zero1_mta_design(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan), flags)
 

@@ -15,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzero1.so")
 SOURCES = [os.path.join(HERE, "csrc", "api.cpp"), os.path.join(HERE, "csrc", "kernels.hip")]
+# bandwidth calibration kernels used by bench.py (not part of the step library)
+CALIB_LIB = os.path.join(HERE, "libzero1_calib.so")
+CALIB_SOURCES = [os.path.join(HERE, "csrc", "calib.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,15 +25,21 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _hipcc(sources, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libzero1.so and the calibration library (always recompiles)."""
+    _hipcc(SOURCES, LIB, verbose)
+    _hipcc(CALIB_SOURCES, CALIB_LIB, verbose)
     return LIB
 
 

@@ -151,21 +151,11 @@ int grid_for(int64_t units, const DevInfo& d, int per_cu)
 
 int64_t tiles(int64_t len, bool /*vec*/) { return (len + kTile - 1) / kTile; }
 
-// Workgroups per CU of the persistent grids.  Defaults are the best measured
-// on MI355X; ZERO1_REDUCE_PER_CU / ZERO1_UPDATE_PER_CU override them (tuning).
-int env_int(const char* name, int dflt)
-{
-    const char* s = std::getenv(name);
-    return (s && *s) ? std::atoi(s) : dflt;
-}
-const int kReducePerCu = env_int("ZERO1_REDUCE_PER_CU", 8);
-
 // Launch shape of the streaming kernels, measured on MI355X (GPT-2 small and
 // Llama-7B W=8 shards, 7e9 W=1): up to a few thousand units, one workgroup
 // per unit with a plain stride is best; past that, a persistent grid of 8
 // workgroups per CU with each XCD walking its own contiguous eighth of the
-// units wins by 2-4%.  ZERO1_UPDATE_PER_CU, ZERO1_REDUCE_SPLIT and
-// ZERO1_UPDATE_SPLIT (1 or 8) override (tuning).
+// units wins by 2-4%.
 struct Shape {
     int grid;
     int split;
@@ -173,30 +163,23 @@ struct Shape {
 
 Shape update_shape(int64_t units, const DevInfo& d)
 {
-    static const int per_cu = env_int("ZERO1_UPDATE_PER_CU", -1);
-    static const int split_env = env_int("ZERO1_UPDATE_SPLIT", 0);
     const bool big = units > kMaxPartials;
-    const int pc = per_cu >= 0 ? per_cu : (big ? 8 : 0);
-    const int split = split_env ? (split_env >= 8 ? 8 : 1) : (big ? 8 : 1);
-    return Shape{grid_for(units, d, pc), split};
+    return Shape{grid_for(units, d, big ? kUpdatePerCu : 0), big ? 8 : 1};
 }
 
 Shape reduce_shape(int64_t tiles, const DevInfo& d)
 {
-    static const int split_env = env_int("ZERO1_REDUCE_SPLIT", 0);
     const int grid = grid_for(tiles, d, kReducePerCu);
-    const int split = split_env ? (split_env >= 8 ? 8 : 1) : (tiles >= 16 * (int64_t)grid ? 8 : 1);
-    return Shape{grid, split};
+    return Shape{grid, tiles >= 16 * (int64_t)grid ? 8 : 1};
 }
 
-// The reduce stores g with the non-temporal hint when g is larger than this
-// (it cannot stay in the 256 MB MALL until the update reads it back; measured
-// 3-6% faster reduce at the 7.5e9/64 and Llama-7B/8 shards, 5% slower update
-// at the GPT-2-small shard if applied there).  ZERO1_G_NT_MB overrides (tuning).
+// The reduce stores g with the non-temporal hint when g is larger than
+// kGNtBytes (it cannot stay in the 256 MB MALL until the update reads it back;
+// measured 3-6% faster reduce at the 7.5e9/64 and Llama-7B/8 shards, 5% slower
+// update at the GPT-2-small shard if applied there).
 bool g_store_nt(int64_t g_elems)
 {
-    static const int mb = env_int("ZERO1_G_NT_MB", 128);
-    return (double)g_elems * sizeof(float) > (double)mb * 1048576.0;
+    return (double)g_elems * sizeof(float) > (double)kGNtBytes;
 }
 
 // ------------------------------------------------------------------ checks
@@ -230,7 +213,7 @@ zero1_status check_grads(const uint16_t* const* grads, int W, int64_t begin, int
     return ZERO1_OK;
 }
 
-constexpr uint32_t kAllFlags = ZERO1_SUM_ONLY | ZERO1_MV_BF16 | ZERO1_RECOMPUTE_G | ZERO1_STORE_G | ZERO1_ONCHIP |
+constexpr uint32_t kAllFlags = ZERO1_SUM_ONLY | ZERO1_MV_BF16 | ZERO1_RECOMPUTE_G | ZERO1_STORE_G |
                                ZERO1_DECAY_FIRST | ZERO1_CLIP_EPS | ZERO1_G_BF16;
 
 zero1_status check_flags(uint32_t flags, uint32_t allowed, const char* fn)
@@ -468,17 +451,8 @@ zero1_status zero1_adamw_step(const float* g, const uint16_t* const* grads, int 
 }
 
 // ------------------------------------------------------------------ multi-tensor
-// Elements per multi-tensor chunk (a multiple of the 2048-element tile);
-// ZERO1_CHUNK_ELEMS overrides the default (tuning).
-static int64_t plan_chunk_elems()
-{
-    static const int64_t c = [] {
-        int64_t v = env_int("ZERO1_CHUNK_ELEMS", kChunkElems);
-        v = (v + kTile - 1) / kTile * kTile;
-        return v < kTile ? (int64_t)kTile : (v > (1 << 20) ? (int64_t)(1 << 20) : v);
-    }();
-    return c;
-}
+// Elements per multi-tensor chunk: one 2048-element tile.
+static int64_t plan_chunk_elems() { return kChunkElems; }
 
 size_t zero1_mta_table_bytes(const zero1_piece* pieces, int n_pieces)
 {
@@ -569,30 +543,9 @@ zero1_status zero1_mta_plan(const zero1_piece* pieces, int n_pieces, uint32_t fl
 
 static bool use_store_g(uint32_t flags, int W)
 {
-    if (flags & ZERO1_ONCHIP) return false;
     if (flags & ZERO1_STORE_G) return true;
     if (flags & ZERO1_RECOMPUTE_G) return false;
     return W > 4;   // 2W+34 bytes/param beats 4W+26 once W > 4
-}
-
-// Single-launch design: the smallest K (tiles held per workgroup) whose
-// co-resident grid holds every chunk.  Returns K and the grid, or 0.
-static int pick_onchip(const zero1_plan* plan, const DevInfo& d, int& grid)
-{
-    if (plan->chunk_elems != kTile) return 0;
-    int ks[8];
-    const int n = onchip_variants(ks, 8);
-    for (int i = 0; i < n; ++i) {
-        int per_cu = 0;
-        if (onchip_max_blocks(ks[i], (plan->flags & ZERO1_MV_BF16) != 0, &per_cu) != hipSuccess || per_cu < 1)
-            continue;
-        int64_t cap = std::min<int64_t>((int64_t)per_cu * d.cus, kMaxPartials);
-        if ((int64_t)plan->n_chunks <= (int64_t)ks[i] * cap) {
-            grid = (int)std::min<int64_t>(cap, plan->n_chunks);
-            return ks[i];
-        }
-    }
-    return 0;
 }
 
 size_t zero1_mta_workspace_bytes(const zero1_plan* plan, int W, uint32_t flags)
@@ -608,9 +561,8 @@ static zero1_status mta_common(const uint16_t* const* grads, int W, int64_t begi
 {
     zero1_status st;
     if (!plan || !plan->table) return fail(ZERO1_EINVAL, "plan is NULL or has no table");
-    const uint32_t designs = flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
-    if (designs & (designs - 1))
-        return fail(ZERO1_EINVAL, "ZERO1_STORE_G, ZERO1_RECOMPUTE_G and ZERO1_ONCHIP are exclusive");
+    if ((flags & ZERO1_STORE_G) && (flags & ZERO1_RECOMPUTE_G))
+        return fail(ZERO1_EINVAL, "ZERO1_STORE_G and ZERO1_RECOMPUTE_G are exclusive");
     if ((st = check_grads(grads, W, begin, plan->shard_len, r, flags, vec))) return st;
     vec = vec && plan->aligned;
     store_g = use_store_g(flags, W);
@@ -628,7 +580,6 @@ zero1_status zero1_mta_reduce(const uint16_t* const* grads, int W, int64_t begin
     DevInfo d;
     Ws w;
     if (!sumsq_out) return fail(ZERO1_EINVAL, "sumsq_out is NULL");
-    if (flags & ZERO1_ONCHIP) return fail(ZERO1_EINVAL, "ZERO1_ONCHIP applies to zero1_mta_step only");
     zero1_status st = mta_common(grads, W, begin, plan, flags, ws, ws_bytes, r, vec, store_g, d, w);
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -651,7 +602,7 @@ zero1_status zero1_mta_reduce_range(const uint16_t* const* grads, int W, const z
     if (lo < 0 || hi < lo || hi > plan->shard_len)
         return fail(ZERO1_EINVAL, "range [%lld, %lld) is not inside the shard [0, %lld)", (long long)lo,
                     (long long)hi, (long long)plan->shard_len);
-    if (flags & (ZERO1_RECOMPUTE_G | ZERO1_ONCHIP))
+    if (flags & ZERO1_RECOMPUTE_G)
         return fail(ZERO1_EINVAL, "zero1_mta_reduce_range stores g: it pairs with ZERO1_STORE_G only");
     Reduce r;
     bool vec = false;
@@ -693,7 +644,6 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
     if ((st = check_hparams(hp))) return st;
     if (n_ranks < 1) return fail(ZERO1_EINVAL, "n_ranks=%d must be >= 1", n_ranks);
     if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
-    if (flags & ZERO1_ONCHIP) return fail(ZERO1_EINVAL, "ZERO1_ONCHIP applies to zero1_mta_step only");
     Reduce r;
     bool vec = false, store_g = false;
     DevInfo d;
@@ -714,20 +664,10 @@ zero1_status zero1_mta_update(const uint16_t* const* grads, int W, int64_t begin
 int zero1_mta_design(const uint16_t* const* grads, int W, int64_t begin, const zero1_plan* plan, uint32_t flags)
 {
     if (!plan || !plan->table) return 0;
-    const uint32_t designs = flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
-    if (designs & (designs - 1)) return 0;
+    if ((flags & ZERO1_STORE_G) && (flags & ZERO1_RECOMPUTE_G)) return 0;
     Reduce r;
     bool vec = false;
     if (check_grads(grads, W, begin, plan->shard_len, r, 0, vec) != ZERO1_OK) return 0;
-    vec = vec && plan->aligned;
-    if (flags & ZERO1_STORE_G) return ZERO1_STORE_G;
-    if (flags & ZERO1_RECOMPUTE_G) return ZERO1_RECOMPUTE_G;
-    if (flags & ZERO1_ONCHIP) {
-        DevInfo d;
-        if (current_device(d) != ZERO1_OK) return 0;
-        int grid = 0;
-        return (vec && pick_onchip(plan, d, grid) > 0) ? (int)ZERO1_ONCHIP : 0;
-    }
     return use_store_g(flags, W) ? ZERO1_STORE_G : ZERO1_RECOMPUTE_G;
 }
 
@@ -742,31 +682,6 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin, 
     if (n_ranks < 1 || my_rank < 0 || my_rank >= n_ranks)
         return fail(ZERO1_EINVAL, "my_rank=%d must be in [0, n_ranks=%d)", my_rank, n_ranks);
     if (!rank_sumsq) return fail(ZERO1_EINVAL, "rank_sumsq is NULL");
-    if (flags & ZERO1_ONCHIP) {
-        if (launch_events_pending())
-            return fail(ZERO1_EINVAL, "ZERO1_ONCHIP: the cooperative launch does not take timing events");
-        Reduce r;
-        bool vec = false, store_g = false;
-        DevInfo d;
-        Ws w;
-        if ((st = mta_common(grads, W, begin, plan, flags, ws, ws_bytes, r, vec, store_g, d, w))) return st;
-        int grid = 0;
-        const int k = vec ? pick_onchip(plan, d, grid) : 0;
-        if (k > 0) {
-            hipStream_t s = static_cast<hipStream_t>(stream);
-            const char* tb = static_cast<const char*>(plan->table);
-            const PieceDesc* pd = reinterpret_cast<const PieceDesc*>(tb);
-            const ChunkDesc* cd =
-                reinterpret_cast<const ChunkDesc*>(tb + round_up(sizeof(PieceDesc) * plan->n_pieces, 256));
-            Z1_HIP(launch_onchip(k, r, pd, cd, plan->n_chunks, (plan->flags & ZERO1_MV_BF16) != 0, scalars(hp, flags),
-                                 w.partials, rank_sumsq, n_ranks, my_rank, hp->max_norm,
-                                 (flags & ZERO1_CLIP_EPS) ? 1 : 0, reinterpret_cast<NormInfo*>(info_out), grid, s));
-            return finish(s);
-        }
-        return fail(ZERO1_EINVAL, "ZERO1_ONCHIP: the shard (%lld elements, %d chunks) does not fit in one "
-                        "co-resident grid, or its buffers are not 16-byte aligned", (long long)plan->shard_len,
-                        plan->n_chunks);
-    }
     if ((st = zero1_mta_reduce(grads, W, begin, plan, rank_sumsq + my_rank, flags, ws, ws_bytes, stream))) return st;
     return zero1_mta_update(grads, W, begin, plan, hp, rank_sumsq, n_ranks, flags, info_out, ws, ws_bytes, stream);
 }
@@ -804,9 +719,8 @@ zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout
     if (!req || !out) return fail(ZERO1_EINVAL, "request or layout is NULL");
     const zero1_arena_request& q = *req;
     if (zero1_status fs = check_flags(q.flags, kAllFlags, "zero1_arena_plan")) return fs;
-    const uint32_t designs = q.flags & (ZERO1_STORE_G | ZERO1_RECOMPUTE_G | ZERO1_ONCHIP);
-    if (designs & (designs - 1))
-        return fail(ZERO1_EINVAL, "ZERO1_STORE_G, ZERO1_RECOMPUTE_G and ZERO1_ONCHIP are exclusive");
+    if ((q.flags & ZERO1_STORE_G) && (q.flags & ZERO1_RECOMPUTE_G))
+        return fail(ZERO1_EINVAL, "ZERO1_STORE_G and ZERO1_RECOMPUTE_G are exclusive");
     if (q.shard_len < 1) return fail(ZERO1_EINVAL, "shard_len=%lld must be >= 1", (long long)q.shard_len);
     if (q.W < 1 || q.W > kMaxW) return fail(ZERO1_EINVAL, "W=%d must be in [1, %d]", q.W, kMaxW);
     if (q.grad_offset < 0 || q.grad_elems < q.grad_offset + q.shard_len)
@@ -839,10 +753,7 @@ zero1_status zero1_arena_plan(const zero1_arena_request* req, zero1_arena_layout
     // the workspace when it is not slot 0
     size_t tail = (size_t)(store_g ? q.W : q.W - 1) * grad_bytes + (store_g ? 0 : round_up(ws_bytes, unit));
     const size_t fixed = base + round_up(slot[4].after, unit) + tail;   // everything but 4 D
-    // ZERO1_ARENA_SPACING_MIB overrides the preferred spacing (tuning)
-    static const int spacing_mib = env_int("ZERO1_ARENA_SPACING_MIB", 0);
-    const size_t preferred = spacing_mib > 0 ? round_up((size_t)spacing_mib << 20, unit) : ZERO1_ARENA_SPACING;
-    size_t d = std::max(d_min, preferred);
+    size_t d = std::max(d_min, (size_t)ZERO1_ARENA_SPACING);
     if (fixed + 4 * d > q.capacity) {
         if (q.capacity < fixed + 4 * d_min)
             return fail(ZERO1_EINVAL, "capacity %zu bytes is below the packed layout's %zu", q.capacity,

@@ -15,6 +15,23 @@ constexpr int kTile = 2048;         // elements per workgroup tile: 256 lanes x 
 constexpr int kMaxPartials = 8192;  // capacity of the per-workgroup norm partials
 constexpr int kChunkElems = 2048;   // multi-tensor chunk: one tile
 
+// Launch shape and cache-policy thresholds, fixed at build time (the values
+// measured best on MI355X).  The grid shapes decide how the fp64 sum of
+// squares is split into partials, so they are constants of the library, not
+// run-time settings: the same build gives the same bits in every process.
+#ifndef Z1_REDUCE_PER_CU
+#define Z1_REDUCE_PER_CU 8          // reduce: persistent grid of 8 workgroups per CU
+#endif
+#ifndef Z1_UPDATE_PER_CU
+#define Z1_UPDATE_PER_CU 8          // update past kMaxPartials units: 8 workgroups per CU
+#endif
+#ifndef Z1_G_NT_BYTES
+#define Z1_G_NT_BYTES (128ll << 20) // g larger than this is stored non-temporally
+#endif
+constexpr int kReducePerCu = Z1_REDUCE_PER_CU;
+constexpr int kUpdatePerCu = Z1_UPDATE_PER_CU;
+constexpr long long kGNtBytes = Z1_G_NT_BYTES;
+
 // W gradient slice pointers, passed by value in the kernel arguments (1 KiB).
 struct GradPtrs {
     const uint16_t* p[kMaxW];
@@ -76,7 +93,6 @@ struct ChunkDesc {
 // (zero1_time_next_launch): the next kernel the launchers below start takes
 // the events (start and stop stamped by its own dispatch) and clears them.
 void set_launch_events(hipEvent_t start, hipEvent_t stop);
-bool launch_events_pending();
 
 // ---- launchers (kernels.hip); each returns the launch's status.
 // Phase 1: g = reduce(slices) over [0, len); optional fp32 store of g and one
@@ -106,13 +122,5 @@ hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pi
                             bool mv_bf16, const Scal& sc, const double* rank_sumsq,
                             int n_ranks, double max_norm, int clip_eps, NormInfo* info_out,
                             int nblocks, int split, hipStream_t s);
-// Single-launch step (cooperative grid barrier) for shards whose reduced
-// gradient fits in registers: K tiles per workgroup.
-int onchip_variants(int* ks, int max_n);
-hipError_t onchip_max_blocks(int k, bool mv_bf16, int* blocks_per_cu);
-hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks, int n_chunks,
-                         bool mv_bf16, const Scal& sc, double* partials, double* rank_sumsq, int n_ranks,
-                         int my_rank, double max_norm, int clip_eps, NormInfo* info_out, int nblocks,
-                         hipStream_t s);
 
 }  // namespace z1

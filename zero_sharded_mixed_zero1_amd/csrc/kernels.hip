@@ -23,9 +23,9 @@
 //   * Tiles that run past the end, and shards whose pointers are not 16-byte
 //     aligned, take an element path (lane t handles t, t+256, ...).
 //
-// Arithmetic contract (the page's AdamW code on "并行训练", section
-// "一张卡上装了什么：混合精度与 AdamW", applied one binary32 operation at a time):
-// built with -ffp-contract=off and the pragma below, so no multiply-add is
+// Arithmetic contract: AdamW with the folded bias correction and the decay
+// after the Adam move, as "并行训练" defines it in "一张卡上装了什么：混合精度与
+// AdamW", evaluated one binary32 operation at a time: built with -ffp-contract=off and the pragma below, so no multiply-add is
 // fused; fp32 '/' and sqrtf are the correctly rounded HIP defaults; subnormals
 // are kept.  fp64 is used only for sums of squares (each square is exact in
 // fp64, so fma(x, x, acc) rounds exactly like acc + x*x).
@@ -36,7 +36,6 @@
 // partials by another (finalize_kernel: strided lane sums, then an LDS
 // halving tree), so a rerun with the same launch shape reproduces every bit,
 // including the norm.
-#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -536,7 +535,9 @@ __device__ __forceinline__ void block_clip(const ClipArgs& ca, bool& clip, float
 }
 
 // ------------------------------------------------------------- phase 2
-// One element of AdamW in the page's order: moments, update, then decay.
+// One element of AdamW: m = b1 m + a1 g, v = b2 v + a2 (g g), then the
+// master moves by sigma m / (sqrt(v) + eps) and is multiplied by the decay
+// factor (decay after the move; decay_first swaps the two).
 __device__ __forceinline__ void adamw_elem(float g, float& p, float& m, float& v, const Scal& c)
 {
     const float mn = c.b1 * m + c.a1 * g;
@@ -657,8 +658,19 @@ __global__ __launch_bounds__(kThreads) void adamw_flat_kernel(Span sp, Reduce r,
     }
 }
 
+// Span of one chunk's piece, starting at the chunk.
 template <bool MVBF16>
-__device__ __forceinline__ Span chunk_span(const PieceDesc& pc, const ChunkDesc& ch);
+__device__ __forceinline__ Span chunk_span(const PieceDesc& pc, const ChunkDesc& ch)
+{
+    const size_t mvb = MVBF16 ? 2 : 4;
+    Span sp;
+    sp.g = nullptr;
+    sp.master = pc.master + ch.offset;
+    sp.m = static_cast<char*>(pc.m) + mvb * ch.offset;
+    sp.v = static_cast<char*>(pc.v) + mvb * ch.offset;
+    sp.param = pc.param + ch.offset;
+    return sp;
+}
 
 template <bool VEC, int GSRC, bool MVBF16>
 __global__ __launch_bounds__(kThreads) void adamw_mta_kernel(const float* __restrict__ g, Reduce r,
@@ -680,119 +692,6 @@ __global__ __launch_bounds__(kThreads) void adamw_mta_kernel(const float* __rest
         for (int sub = 0; sub < ch.len; sub += kTile) {
             const int n = ch.len - sub < kTile ? ch.len - sub : kTile;
             update_tile<VEC, GSRC, MVBF16>(sp, r, g0 + sub, sub, n, c, clip, coef);
-        }
-    }
-}
-
-// ------------------------------------------------------------- single launch
-// The whole step in one cooperative launch for shards whose reduced gradient
-// fits in the register file: every workgroup reduces up to K one-tile chunks
-// and keeps their g in registers (8 per lane per chunk), publishes its fp64
-// partial, waits at a grid barrier, forms this rank's sum of squares from all
-// partials (every workgroup in the same fixed order), the global norm and the
-// clip decision, and then updates the same chunks from the registers.  The
-// reduced gradient never touches HBM: traffic is exactly 2W+26 bytes/param.
-struct OnchipArgs {
-    double* partials;       // gridDim.x entries
-    double* rank_sumsq;     // n_ranks entries; entry my_rank is written
-    int n_ranks;
-    int my_rank;
-    double max_norm;
-    int clip_eps;
-    NormInfo* info_out;     // may be null
-};
-
-// Span of one chunk's piece, starting at the chunk.
-template <bool MVBF16>
-__device__ __forceinline__ Span chunk_span(const PieceDesc& pc, const ChunkDesc& ch)
-{
-    const size_t mvb = MVBF16 ? 2 : 4;
-    Span sp;
-    sp.g = nullptr;
-    sp.master = pc.master + ch.offset;
-    sp.m = static_cast<char*>(pc.m) + mvb * ch.offset;
-    sp.v = static_cast<char*>(pc.v) + mvb * ch.offset;
-    sp.param = pc.param + ch.offset;
-    return sp;
-}
-
-template <int K, int MINW, bool MVBF16>
-__global__ __launch_bounds__(kThreads, MINW) void onchip_step_kernel(Reduce r, const PieceDesc* __restrict__ pieces,
-                                                                      const ChunkDesc* __restrict__ chunks,
-                                                                      int n_chunks, Scal c, OnchipArgs oa)
-{
-    use_device_scalars(c, oa.max_norm);
-    float greg[K][8];
-    double acc = 0.0;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int ci = blockIdx.x + k * gridDim.x;
-        if (ci < n_chunks) {
-            const ChunkDesc ch = chunks[ci];
-            const int64_t g0 = pieces[ch.piece].shard_offset + ch.offset;
-            if (ch.len == kTile) {
-                reduce8(r, g0, greg[k]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc = fma((double)greg[k][j], (double)greg[k][j], acc);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int j = threadIdx.x + kThreads * i;
-                    greg[k][i] = 0.0f;
-                    if (j < ch.len) {
-                        greg[k][i] = reduce1(r, g0 + j);
-                        acc = fma((double)greg[k][i], (double)greg[k][i], acc);
-                    }
-                }
-            }
-        }
-    }
-    const double b = block_sum(acc);
-    if (threadIdx.x == 0) oa.partials[blockIdx.x] = b;
-
-    cooperative_groups::this_grid().sync();
-
-    // this rank's sum of squares: the partials in the fixed order of finalize_kernel
-    __shared__ double sh[kThreads];
-    __shared__ NormInfo shi;
-    double a = 0.0;
-    for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) a = a + oa.partials[i];
-    sh[threadIdx.x] = a;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + s];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        const double q_r = sh[0];
-        double tot = 0.0;
-        for (int q = 0; q < oa.n_ranks; ++q) tot = tot + (q == oa.my_rank ? q_r : oa.rank_sumsq[q]);
-        const NormInfo ni = norm_info(tot, oa.max_norm, oa.clip_eps);
-        shi = ni;
-        if (blockIdx.x == 0) {
-            oa.rank_sumsq[oa.my_rank] = q_r;     // no workgroup reads this entry
-            if (oa.info_out) *oa.info_out = ni;
-        }
-    }
-    __syncthreads();
-    const bool clip = shi.clip != 0;
-    const float coef = shi.clip_coef;
-
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int ci = blockIdx.x + k * gridDim.x;
-        if (ci < n_chunks) {
-            const ChunkDesc ch = chunks[ci];
-            const Span sp = chunk_span<MVBF16>(pieces[ch.piece], ch);
-            if (ch.len == kTile) {
-                update8<MVBF16>(sp, 0, greg[k], c, clip, coef);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int j = threadIdx.x + kThreads * i;
-                    if (j < ch.len) update1<MVBF16>(sp, j, greg[k][i], c, clip, coef);
-                }
-            }
         }
     }
 }
@@ -837,8 +736,6 @@ void set_launch_events(hipEvent_t start, hipEvent_t stop)
     t_ev_start = start;
     t_ev_stop = stop;
 }
-
-bool launch_events_pending() { return t_ev_start || t_ev_stop; }
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, double* partials,
@@ -928,50 +825,6 @@ hipError_t launch_adamw_mta(const float* g, const Reduce& r, const PieceDesc* pi
     }
 #undef Z1_MTA
     return e;
-}
-
-// K tiles held per workgroup and the minimum waves per SIMD the register
-// budget is sized for (K=8: 64 registers of g per lane, 4 waves/SIMD).
-#define Z1_ONCHIP_VARIANTS(X) X(2, 8) X(4, 5) X(8, 4) X(12, 3)
-
-static const void* onchip_fn(int k, bool mv_bf16)
-{
-#define Z1_FN(K, MW) if (k == K) return mv_bf16 ? (const void*)onchip_step_kernel<K, MW, true> : (const void*)onchip_step_kernel<K, MW, false>;
-    Z1_ONCHIP_VARIANTS(Z1_FN)
-#undef Z1_FN
-    return nullptr;
-}
-
-int onchip_variants(int* ks, int max_n)
-{
-    int n = 0;
-#define Z1_K(K, MW) if (n < max_n) ks[n++] = K;
-    Z1_ONCHIP_VARIANTS(Z1_K)
-#undef Z1_K
-    return n;
-}
-
-hipError_t onchip_max_blocks(int k, bool mv_bf16, int* blocks_per_cu)
-{
-    const void* f = onchip_fn(k, mv_bf16);
-    if (!f) return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
-}
-
-hipError_t launch_onchip(int k, const Reduce& r, const PieceDesc* pieces, const ChunkDesc* chunks, int n_chunks,
-                         bool mv_bf16, const Scal& sc, double* partials, double* rank_sumsq, int n_ranks, int my_rank,
-                         double max_norm, int clip_eps, NormInfo* info_out, int nblocks, hipStream_t s)
-{
-    const void* f = onchip_fn(k, mv_bf16);
-    if (!f) return hipErrorInvalidValue;
-    Reduce rr = r;
-    const PieceDesc* pd = pieces;
-    const ChunkDesc* cd = chunks;
-    int nc = n_chunks;
-    Scal cc = sc;
-    OnchipArgs oa{partials, rank_sumsq, n_ranks, my_rank, max_norm, clip_eps, info_out};
-    void* args[] = {&rr, &pd, &cd, &nc, &cc, &oa};
-    return hipLaunchCooperativeKernel(f, dim3(nblocks), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace z1
