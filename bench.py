@@ -102,23 +102,45 @@ def cal_lib():
             raise ImportError(f"{path} is not built: run __graft_entry__.build()")
         L = ctypes.CDLL(path)
         P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
-        L.zcal_stream.argtypes = [P, P, i32, P, P, i32, i64, i32, i32, P, P]
+        L.zcal_stream.argtypes = [P, P, P, i32, P, P, P, i32, i64, i32, i32, i32, i32, P, P]
         L.zcal_stream.restype = i32
         _cal = L
     return _cal
 
 
-def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream):
-    """One calibration pass: rd/wr are [(device address, bytes per element)];
-    every stream must hold n_tiles * 2048 elements from its address."""
+def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream, tiles_in_flight=1, wide=0):
+    """One calibration pass.  rd: [(device address, bytes per element, plain
+    loads?)]; wr: [(device address, bytes per element, sc1 stores?)]; every
+    stream must hold n_tiles * 2048 elements from its address."""
     R, Wn = len(rd), len(wr)
-    rp = (ctypes.c_void_p * max(R, 1))(*[a for a, _ in rd])
-    rb = (ctypes.c_int * max(R, 1))(*[b for _, b in rd])
-    wp = (ctypes.c_void_p * max(Wn, 1))(*[a for a, _ in wr])
-    wb = (ctypes.c_int * max(Wn, 1))(*[b for _, b in wr])
-    st = cal_lib().zcal_stream(rp, rb, R, wp, wb, Wn, n_tiles, grid, split, sink, stream)
+
+    def arr(t, vals):
+        return (t * max(len(vals), 1))(*vals)
+
+    st = cal_lib().zcal_stream(arr(ctypes.c_void_p, [x[0] for x in rd]), arr(ctypes.c_int, [x[1] for x in rd]),
+                               arr(ctypes.c_int, [int(x[2]) for x in rd]), R,
+                               arr(ctypes.c_void_p, [x[0] for x in wr]), arr(ctypes.c_int, [x[1] for x in wr]),
+                               arr(ctypes.c_int, [int(x[2]) for x in wr]), Wn,
+                               n_tiles, tiles_in_flight, wide, grid, split, sink, stream)
     if st != 0:
         raise RuntimeError(f"zcal_stream failed with status {st}")
+
+
+def best_calibration(torch, rd, wr, n_tiles, grid, split, sink, stream, reps=5):
+    """The fastest calibration pass over U (tiles whose loads are issued
+    together) in {1, 2, 4, 8} with at most eight (tile, stream) loads in
+    flight: (ms, U)."""
+    best = None
+    for U in (1, 2, 4, 8):
+        if U > 1 and U * max(len(rd), 1) > 8:
+            continue
+        fn = lambda: zcal_stream(rd, wr, n_tiles, grid, split, sink, stream, U)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        ms = timed_passes(torch, fn, reps)
+        if best is None or ms < best[0]:
+            best = (ms, U)
+    return best
 
 
 def timed_passes(torch, fn, reps):
@@ -306,31 +328,38 @@ def ceilings(torch, z, cfg, st, store_g, cus):
     if n_tiles == 0:
         return None
     grads = [al(g.data_ptr() + 2 * c.begin) for g in c.grads]
-    state_rd = [(al(c.master.data_ptr()), 4), (al(c.m.data_ptr()), mvb), (al(c.v.data_ptr()), mvb)]
-    state_wr = state_rd + [(al(c.shard_params.data_ptr()), 2)]
+    state = [(al(c.master.data_ptr()), 4), (al(c.m.data_ptr()), mvb), (al(c.v.data_ptr()), mvb)]
+    state_rd = [(a, b, False) for a, b in state]
+    state_wr = [(a, b, False) for a, b in state] + [(al(c.shard_params.data_ptr()), 2, False)]
     if store_g:
-        g = al(c.ws.data_ptr() + 256 + 8 * 8192)      # the g region of the workspace
-        red_rd, red_wr = [(a, 2) for a in grads], [(g, 4)]
-        upd_rd = [(g, 4)] + state_rd
+        # the g region of the workspace; a g that fits the MALL is stored with
+        # sc1 and read back with plain loads, as the step kernels do
+        g = al(c.ws.data_ptr() + 256 + 8 * 8192)
+        small = 4 * S <= (128 << 20)
+        red_rd, red_wr = [(a, 2, False) for a in grads], [(g, 4, small)]
+        upd_rd = [(g, 4, small)] + state_rd
     else:
-        red_rd, red_wr = [(a, 2) for a in grads], []
-        upd_rd = [(a, 2) for a in grads] + state_rd
+        red_rd, red_wr = [(a, 2, False) for a in grads], []
+        upd_rd = [(a, 2, False) for a in grads] + state_rd
     sink = torch.zeros(8192, dtype=torch.int32, device=c.master.device)
     stream = torch.cuda.current_stream().cuda_stream
     rg, rs = launch_shape(n_tiles, cus, 8, lambda u, n: u >= 16 * n)
     ug, us = launch_shape(n_tiles, cus, 8 if n_tiles > 8192 else 0, lambda u, n: u > 8192)
-
-    def one(rd, wr, grid, split):
-        zcal_stream(rd, wr, n_tiles, grid, split, sink.data_ptr(), stream)
-
     out = {}
-    for name, rd, wr, grid, split in (("reduce", red_rd, red_wr, rg, rs), ("update", upd_rd, state_wr, ug, us)):
-        one(rd, wr, grid, split)
-        torch.cuda.synchronize()
-        ms = timed_passes(torch, lambda: one(rd, wr, grid, split), 5)
-        nbytes = n_tiles * 2048 * (sum(b for _, b in rd) + sum(b for _, b in wr))
+    passes = (("reduce", red_rd, red_wr, rg, rs), ("update", upd_rd, state_wr, ug, us))
+    for name, rd, wr, grid, split in passes:
+        ms, U = best_calibration(torch, rd, wr, n_tiles, grid, split, sink.data_ptr(), stream)
+        nbytes = n_tiles * 2048 * (sum(x[1] for x in rd) + sum(x[1] for x in wr))
         out[name] = {"ms": ms, "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
-                     "shard_ms": ms * S / (n_tiles * 2048)}
+                     "shard_ms": ms * S / (n_tiles * 2048), "tiles_in_flight": U}
+
+    # the two passes back to back, as the step runs them (the update finds
+    # in the MALL what the reduce's sc1 stores left there)
+    def pair():
+        for name, rd, wr, grid, split in passes:
+            zcal_stream(rd, wr, n_tiles, grid, split, sink.data_ptr(), stream, out[name]["tiles_in_flight"])
+
+    out["step_shard_ms"] = timed_passes(torch, pair, 5) * S / (n_tiles * 2048)
     return out
 
 
@@ -414,7 +443,8 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
             kk["ceiling_ms"] = cal[k]["shard_ms"]
             kk["ceiling_moved_GBps"] = cal[k]["GBps"]
             kk["frac_of_ceiling"] = cal[k]["shard_ms"] / kk["ms"]
-        res["ceiling_ms_per_step"] = cal["reduce"]["shard_ms"] + cal["update"]["shard_ms"]
+            kk["ceiling_tiles_in_flight"] = cal[k]["tiles_in_flight"]
+        res["ceiling_ms_per_step"] = cal["step_shard_ms"]
     del st, c0
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -667,18 +697,18 @@ def calibrate(torch, dev, gib=4, spacing_gib=40):
                 arena = torch.empty(max(o + sz for o, sz in zip(offs, sizes)), dtype=torch.uint8, device=dev)
                 addrs = [arena.data_ptr() + o for o in offs]
                 bufs = [arena]
-            for t in bufs:
-                t.fill_(0x3c)
-            rd = [(addrs[i], b) for i, b in rspec]
-            wr = [(addrs[i], b) for i, b in wspec]
-            fn = lambda: zcal_stream(rd, wr, n_tiles, grid, split, sink.data_ptr(), stream)  # noqa: E731
-            fn()
-            torch.cuda.synchronize()
-            ms = timed_passes(torch, fn, 7)
+            for buf in bufs:
+                buf.fill_(0x3c)
+            del buf
+            rd = [(addrs[i], b, False) for i, b in rspec]
+            wr = [(addrs[i], b, False) for i, b in wspec]
+            ms, U = best_calibration(torch, rd, wr, n_tiles, grid, split, sink.data_ptr(), stream, reps=5)
             nbytes = n_tiles * 2048 * (sum(b for _, b in rspec) + sum(b for _, b in wspec))
             out[f"{layout}_{name}_GBps"] = nbytes / (ms * 1e-3) / 1e9
-            log(f"calibrate {layout} {name}: {out[f'{layout}_{name}_GBps']:.0f} GB/s")
-            del bufs, rd, wr, fn
+            out[f"{layout}_{name}_tiles_in_flight"] = U
+            log(f"calibrate {layout} {name}: {out[f'{layout}_{name}_GBps']:.0f} GB/s (U={U})")
+            del bufs, addrs, rd, wr
+            arena = None
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
     return out

@@ -1,19 +1,29 @@
 // calib.hip -- bandwidth calibration kernels for measurement (libzero1_calib.so).
 //
-// Not part of the optimizer step: these kernels move bytes in the exact access
+// Not part of the optimizer step: these kernels move bytes in the access
 // pattern of the step kernels and compute nothing, so that their time is what
 // HBM delivers for that traffic mix and that placement of the arrays.  A step
-// kernel's time over the matching calibration time is then its efficiency
-// against an achievable ceiling, next to its fraction of the nominal 8 TB/s.
+// kernel's time over the best calibration time for its streams is then its
+// efficiency against an achievable ceiling, next to its fraction of the
+// nominal 8 TB/s.
 //
 // Access pattern (the same as the step kernels): tiles of 2048 elements per
 // 256-lane workgroup; lane l of wave w owns the quads [512w + 4l, +4) and
 // [512w + 256 + 4l, +4) of a tile, so every wave instruction covers one
-// contiguous run (512 B of a 2-byte stream, 1 KiB of a 4-byte one); loads and
-// stores carry the non-temporal hint; read streams are loaded in batches of up
-// to eight before any is used; with split = 8 the tiles are split into eight
-// contiguous parts, one per XCD (workgroup b runs on XCD b % 8), each walked
-// with a stride of that XCD's workgroup count; with split = 1, one grid stride.
+// contiguous run (512 B of a 2-byte stream, 1 KiB of a 4-byte one).  With
+// split = 8 the tiles are split into eight contiguous parts, one per XCD
+// (workgroup b runs on XCD b % 8), each walked with a stride of that XCD's
+// workgroup count; with split = 1, one grid stride.
+//
+// The lane layout can also be eight consecutive elements per lane (one
+// 16-byte access per 2-byte stream) to measure that alternative.
+//
+// Loads in flight: a workgroup takes U of its tiles at a time and issues the
+// loads of up to eight (tile, read stream) pairs before any is used (U = 1 and
+// eight streams per batch is the reduce's pattern; U = 8 with one stream is
+// the few-slice sum-of-squares pass's).  Per stream, the cache policy: reads
+// non-temporal or plain, writes non-temporal or through a buffer descriptor
+// with the sc1 bit (the policies the step kernels use for g).
 //
 // Every read stream is folded into a per-lane XOR (so no load can be dropped)
 // and every write stream receives that XOR, so the bytes moved are exactly
@@ -27,6 +37,8 @@ constexpr int kThreads = 256;
 constexpr int kTile = 2048;
 constexpr int kMaxRd = 128;
 constexpr int kMaxWr = 8;
+constexpr int kBufSc1 = 16;                   // cache-policy operand of buffer stores: sc1
+constexpr int kBufDword3 = 0x00020000;        // gfx9 buffer descriptor word 3 (raw, untyped)
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -35,8 +47,11 @@ struct Streams {
     const void* rd[kMaxRd];
     void* wr[kMaxWr];
     uint8_t rd_bytes[kMaxRd];   // 2 or 4 bytes per element
+    uint8_t rd_plain[kMaxRd];   // 1: plain loads, 0: non-temporal
     uint8_t wr_bytes[kMaxWr];
+    uint8_t wr_sc1[kMaxWr];     // 1: sc1 buffer stores, 0: non-temporal
     int n_rd, n_wr;
+    int wide;                   // lane layout: 0 two quads, 1 eight consecutive elements
 };
 
 template <typename T>
@@ -44,22 +59,35 @@ using gptr = __attribute__((address_space(1))) T*;
 
 __device__ __forceinline__ int quad_a() { return 512 * (int)(threadIdx.x >> 6) + 4 * (int)(threadIdx.x & 63); }
 
-// The lane's 8 elements of one stream in the tile at element e, as four
-// 32-bit words (a 2-byte stream fills words 0-1 of each quad's pair, the
-// upper two are zero), xor-folded into acc.
-__device__ __forceinline__ void ld_fold(const void* base, int bytes, int64_t e, u32x4 (&acc)[2])
+// The two runs of four elements a lane owns in a tile: the quads a and a + 256
+// (each wave instruction covers 512 contiguous elements), or, with the wide
+// layout, the eight consecutive elements [8 t, 8 t + 8) (a 2-byte stream is
+// then one 16-byte access per lane, 1 KiB per wave instruction).
+__device__ __forceinline__ int run0(int wide) { return wide ? 8 * (int)threadIdx.x : quad_a(); }
+__device__ __forceinline__ int run1(int wide) { return wide ? 8 * (int)threadIdx.x + 4 : quad_a() + 256; }
+
+template <typename T>
+__device__ __forceinline__ T ld(const T* p, bool plain)
 {
-    const int a = quad_a();
+    return plain ? *(gptr<const T>)p : __builtin_nontemporal_load((gptr<const T>)p);
+}
+
+// The lane's 8 elements of one stream in the tile at element e, as up to four
+// 32-bit words per quad (a 2-byte stream fills words 0-1), xor-folded into acc.
+__device__ __forceinline__ void ld_fold(const void* base, int bytes, bool plain, int wide, int64_t e,
+                                        u32x4 (&acc)[2])
+{
     if (bytes == 4) {
         const uint32_t* p = static_cast<const uint32_t*>(base) + e;
-        const u32x4 x = __builtin_nontemporal_load((gptr<const u32x4>)(p + a));
-        const u32x4 y = __builtin_nontemporal_load((gptr<const u32x4>)(p + a + 256));
-        acc[0] ^= x;
-        acc[1] ^= y;
+        acc[0] ^= ld(reinterpret_cast<const u32x4*>(p + run0(wide)), plain);
+        acc[1] ^= ld(reinterpret_cast<const u32x4*>(p + run1(wide)), plain);
+    } else if (wide) {
+        const uint16_t* p = static_cast<const uint16_t*>(base) + e;
+        acc[0] ^= ld(reinterpret_cast<const u32x4*>(p + run0(1)), plain);
     } else {
         const uint16_t* p = static_cast<const uint16_t*>(base) + e;
-        const u32x2 x = __builtin_nontemporal_load((gptr<const u32x2>)(p + a));
-        const u32x2 y = __builtin_nontemporal_load((gptr<const u32x2>)(p + a + 256));
+        const u32x2 x = ld(reinterpret_cast<const u32x2*>(p + run0(0)), plain);
+        const u32x2 y = ld(reinterpret_cast<const u32x2*>(p + run1(0)), plain);
         acc[0].x ^= x.x;
         acc[0].y ^= x.y;
         acc[1].x ^= y.x;
@@ -67,48 +95,79 @@ __device__ __forceinline__ void ld_fold(const void* base, int bytes, int64_t e, 
     }
 }
 
-__device__ __forceinline__ void st_acc(void* base, int bytes, int64_t e, const u32x4 (&acc)[2], uint32_t salt)
+__device__ __forceinline__ void st_acc(void* base, int bytes, bool sc1, int wide, int64_t e,
+                                       const u32x4 (&acc)[2], uint32_t salt)
 {
-    const int a = quad_a();
+    const int a = run0(wide), b = run1(wide);
     if (bytes == 4) {
         uint32_t* p = static_cast<uint32_t*>(base) + e;
-        __builtin_nontemporal_store(acc[0] ^ salt, (gptr<u32x4>)(p + a));
-        __builtin_nontemporal_store(acc[1] ^ salt, (gptr<u32x4>)(p + a + 256));
+        const u32x4 x = acc[0] ^ salt, y = acc[1] ^ salt;
+        if (sc1) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(p, 0, kTile * 4, kBufDword3);
+            __builtin_amdgcn_raw_buffer_store_b128(x, rs, a * 4, 0, kBufSc1);
+            __builtin_amdgcn_raw_buffer_store_b128(y, rs, b * 4, 0, kBufSc1);
+        } else {
+            __builtin_nontemporal_store(x, (gptr<u32x4>)(p + a));
+            __builtin_nontemporal_store(y, (gptr<u32x4>)(p + b));
+        }
+    } else if (wide) {
+        uint16_t* p = static_cast<uint16_t*>(base) + e;
+        __builtin_nontemporal_store(acc[0] ^ acc[1] ^ salt, (gptr<u32x4>)(p + a));
     } else {
         uint16_t* p = static_cast<uint16_t*>(base) + e;
         const u32x2 x = {acc[0].x ^ acc[0].z ^ salt, acc[0].y ^ acc[0].w};
         const u32x2 y = {acc[1].x ^ acc[1].z ^ salt, acc[1].y ^ acc[1].w};
         __builtin_nontemporal_store(x, (gptr<u32x2>)(p + a));
-        __builtin_nontemporal_store(y, (gptr<u32x2>)(p + a + 256));
+        __builtin_nontemporal_store(y, (gptr<u32x2>)(p + b));
     }
 }
 
+// U tiles at a time; each batch issues the loads of B = 8 / U streams of all
+// U tiles (8 pairs) before folding them.
+template <int U>
 __global__ __launch_bounds__(kThreads) void stream_kernel(Streams s, int64_t ntiles, int split, uint32_t* sink)
 {
+    constexpr int B = 8 / U;
     const int64_t G = gridDim.x, b = blockIdx.x;
     const int64_t nx = (split > 1 && G % split == 0) ? split : 1;
     const int64_t x = b % nx, per = (ntiles + nx - 1) / nx;
     const int64_t lo = x * per, hi = lo + per < ntiles ? lo + per : ntiles;
+    const int64_t step = G / nx;
     u32x4 tot = {0u, 0u, 0u, 0u};
-    for (int64_t t = lo + b / nx; t < hi; t += G / nx) {
-        const int64_t e = t * kTile;
-        u32x4 acc[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-        // batches of up to eight streams: all loads issued before the folds
-        for (int k0 = 0; k0 < s.n_rd; k0 += 8) {
-            u32x4 part[8][2];
+    for (int64_t t = lo + b / nx; t < hi; t += U * step) {
+        u32x4 acc[U][2];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                part[k][0] = part[k][1] = u32x4{0u, 0u, 0u, 0u};
-                if (k0 + k < s.n_rd) ld_fold(s.rd[k0 + k], s.rd_bytes[k0 + k], e, part[k]);
+        for (int j = 0; j < U; ++j) acc[j][0] = acc[j][1] = u32x4{0u, 0u, 0u, 0u};
+        for (int k0 = 0; k0 < s.n_rd; k0 += B) {
+            u32x4 part[U][B][2];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+#pragma unroll
+                for (int k = 0; k < B; ++k) {
+                    part[j][k][0] = part[j][k][1] = u32x4{0u, 0u, 0u, 0u};
+                    if (k0 + k < s.n_rd && t + j * step < hi)
+                        ld_fold(s.rd[k0 + k], s.rd_bytes[k0 + k], s.rd_plain[k0 + k], s.wide,
+                                (t + j * step) * kTile, part[j][k]);
+                }
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                acc[0] ^= part[k][0];
-                acc[1] ^= part[k][1];
+            for (int j = 0; j < U; ++j) {
+#pragma unroll
+                for (int k = 0; k < B; ++k) {
+                    acc[j][0] ^= part[j][k][0];
+                    acc[j][1] ^= part[j][k][1];
+                }
             }
         }
-        for (int k = 0; k < s.n_wr; ++k) st_acc(s.wr[k], s.wr_bytes[k], e, acc, (uint32_t)k);
-        tot ^= acc[0] ^ acc[1];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (t + j * step < hi) {
+                for (int k = 0; k < s.n_wr; ++k)
+                    st_acc(s.wr[k], s.wr_bytes[k], s.wr_sc1[k], s.wide, (t + j * step) * kTile, acc[j],
+                           (uint32_t)k);
+                tot ^= acc[j][0] ^ acc[j][1];
+            }
+        }
     }
     // keeps the loads of a read-only pass alive; the condition never holds
     // for data that is not crafted for it, so nothing is written in practice
@@ -121,16 +180,25 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Streams s, int64_t nti
 extern "C" {
 
 // One pass over n_tiles * 2048 elements of every stream.
-//   rd[n_rd], rd_bytes[n_rd]: read streams (device pointers, 16-byte aligned)
-//     and their element sizes (2 or 4); n_rd <= 128.
-//   wr[n_wr], wr_bytes[n_wr]: write streams likewise; n_wr <= 8.
+//   rd[n_rd]: read streams (device pointers, 16-byte aligned); rd_bytes: their
+//     element sizes (2 or 4); rd_plain: 1 for plain loads, 0 for
+//     non-temporal ones (NULL: all non-temporal); n_rd <= 128.
+//   wr[n_wr], wr_bytes: write streams likewise; wr_sc1: 1 for sc1 buffer
+//     stores (4-byte streams only), 0 for non-temporal ones (NULL: all
+//     non-temporal); n_wr <= 8.  A write stream may be one of the read
+//     streams (an in-place update).
+//   tiles_in_flight: U in {1, 2, 4, 8} (tiles whose loads are issued together).
+//   wide: 0 for the step kernels' lane layout (two quads 256 elements apart),
+//     1 for eight consecutive elements per lane.
 //   grid, split: workgroups, and 8 (one contiguous part of the tiles per XCD;
 //     grid a multiple of 8) or 1 (a plain grid stride).
 //   sink: grid uint32 words of device memory (written only in a case that
 //     does not occur; it keeps a read-only pass from being optimized away).
+// Every stream must hold n_tiles * 2048 elements from its pointer.
 // Returns 0, 1 for a bad argument, or 2 + the HIP error code of the launch.
-int zcal_stream(const void* const* rd, const int* rd_bytes, int n_rd, void* const* wr, const int* wr_bytes,
-                int n_wr, int64_t n_tiles, int grid, int split, void* sink, void* stream)
+int zcal_stream(const void* const* rd, const int* rd_bytes, const int* rd_plain, int n_rd, void* const* wr,
+                const int* wr_bytes, const int* wr_sc1, int n_wr, int64_t n_tiles, int tiles_in_flight,
+                int wide, int grid, int split, void* sink, void* stream)
 {
     if (n_rd < 0 || n_rd > kMaxRd || n_wr < 0 || n_wr > kMaxWr || n_tiles < 0 || grid < 1 || !sink ||
         (split != 1 && split != 8))
@@ -140,17 +208,28 @@ int zcal_stream(const void* const* rd, const int* rd_bytes, int n_rd, void* cons
         if (!rd[k] || (rd_bytes[k] != 2 && rd_bytes[k] != 4) || reinterpret_cast<uintptr_t>(rd[k]) % 16) return 1;
         s.rd[k] = rd[k];
         s.rd_bytes[k] = (uint8_t)rd_bytes[k];
+        s.rd_plain[k] = (uint8_t)(rd_plain && rd_plain[k] ? 1 : 0);
     }
     for (int k = 0; k < n_wr; ++k) {
         if (!wr[k] || (wr_bytes[k] != 2 && wr_bytes[k] != 4) || reinterpret_cast<uintptr_t>(wr[k]) % 16) return 1;
+        if (wr_sc1 && wr_sc1[k] && wr_bytes[k] != 4) return 1;
         s.wr[k] = wr[k];
         s.wr_bytes[k] = (uint8_t)wr_bytes[k];
+        s.wr_sc1[k] = (uint8_t)(wr_sc1 && wr_sc1[k] ? 1 : 0);
     }
     s.n_rd = n_rd;
     s.n_wr = n_wr;
+    s.wide = wide ? 1 : 0;
     if (n_tiles == 0) return 0;
-    hipLaunchKernelGGL(stream_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), s, n_tiles,
-                       split, static_cast<uint32_t*>(sink));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t* sk = static_cast<uint32_t*>(sink);
+    switch (tiles_in_flight) {
+    case 1: hipLaunchKernelGGL(stream_kernel<1>, dim3(grid), dim3(kThreads), 0, st, s, n_tiles, split, sk); break;
+    case 2: hipLaunchKernelGGL(stream_kernel<2>, dim3(grid), dim3(kThreads), 0, st, s, n_tiles, split, sk); break;
+    case 4: hipLaunchKernelGGL(stream_kernel<4>, dim3(grid), dim3(kThreads), 0, st, s, n_tiles, split, sk); break;
+    case 8: hipLaunchKernelGGL(stream_kernel<8>, dim3(grid), dim3(kThreads), 0, st, s, n_tiles, split, sk); break;
+    default: return 1;
+    }
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 0 : 2 + (int)e;
 }
