@@ -95,6 +95,15 @@ def lib():
         if not os.path.exists(lib_path):
             raise ImportError(f"{lib_path} is not built: run __graft_entry__.build() "
                               "(the HIP library is the only implementation)")
+        # PyTorch ships its own HIP runtime (SONAME libamdhip64.so.7, which its
+        # libraries load by the file name libamdhip64.so).  Loading torch first
+        # lets libzero1's libamdhip64.so.7 resolve to that same copy; loaded the
+        # other way round, the process would hold two HIP runtimes, and the
+        # second to initialise finds no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(lib_path)
         L.zero1_abi_version.argtypes = []
         L.zero1_abi_version.restype = i32
