@@ -340,6 +340,35 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
                             uint32_t flags, zero1_norm_info* info_out,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  zero1_mta_step_static is zero1_mta_step (same arguments, same
+ * kernels, same results bit for bit) with its workspace in a static device
+ * array of the library instead of a caller's buffer.
+ *   - The array holds the workspace of a store-g step of up to
+ *     ZERO1_STATIC_MAX_G_ELEMS shard elements (64 MiB of fp32 g plus 64.25 KiB
+ *     of norm partials and info); every GPU the library runs on holds its own
+ *     copy until the process ends.  A shard whose step needs more (the
+ *     store-g design, chosen by default when W > 4, with a longer shard) is
+ *     rejected with ZERO1_EINVAL before anything is launched; with
+ *     ZERO1_RECOMPUTE_G any shard length fits.
+ *   - The array's device address is looked up once per device, on the first
+ *     call with that device current; the call allocates nothing.
+ *   - Each call writes every byte of the array it reads before reading it,
+ *     so nothing needs to start at zero.  All calls on one GPU share its
+ *     array: calls that overlap in time on one GPU (different streams, or
+ *     several host threads) race and give wrong results.  The caller orders
+ *     them (one stream, or events between streams).
+ *   - The caller still owns the gradients, the plan table, the state
+ *     buffers, rank_sumsq and info_out. */
+#define ZERO1_STATIC_MAX_G_ELEMS 16777216
+zero1_status zero1_mta_step_static(const uint16_t* const* grads, int W, int64_t begin,
+                                   const zero1_plan* plan, const zero1_hparams* hp,
+                                   double* rank_sumsq, int n_ranks, int my_rank,
+                                   uint32_t flags, zero1_norm_info* info_out,
+                                   void* stream);
+
 /* ---------------------------------------------------------------- timing
  * Kernel-scoped timing of the step calls, for profiling.  After this call,
  * the first kernel launched by the calling thread's next call of a step entry

@@ -7,10 +7,11 @@ library is missing, importing the binding functions raises.
 """
 from .binding import (  # noqa: F401
     Zero1Error, HParams, NormInfo, Piece, Plan, ArenaRequest, ArenaLayout, StepScalars,
-    SUM_ONLY, MV_BF16, RECOMPUTE_G, STORE_G, DECAY_FIRST, CLIP_EPS, G_BF16, MAX_W,
+    SUM_ONLY, MV_BF16, RECOMPUTE_G, STORE_G, DECAY_FIRST, CLIP_EPS, G_BF16, MAX_W, STATIC_MAX_G_ELEMS,
     abi_version, last_error, shard_range, workspace_bytes,
     shard_reduce, grad_norm, adamw_step,
-    mta_table_bytes, mta_plan, mta_workspace_bytes, mta_reduce, mta_update, mta_design, mta_step, mta_reduce_range, partials_sum,
+    mta_table_bytes, mta_plan, mta_workspace_bytes, mta_reduce, mta_update, mta_design, mta_step,
+    mta_step_static, mta_reduce_range, partials_sum,
     arena_plan, step_scalars_derive, time_next_launch,
     lib, lib_path,
 )

@@ -23,6 +23,7 @@ DECAY_FIRST = 0x20
 CLIP_EPS = 0x40
 G_BF16 = 0x80
 MAX_W = 128
+STATIC_MAX_G_ELEMS = 16777216
 # the layout of the structures below and the signatures set in lib(); a
 # library that reports another ZERO1_ABI_VERSION is refused at load time
 ABI_VERSION = 4
@@ -145,6 +146,9 @@ def lib():
         L.zero1_mta_step.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
                                      P, i32, i32, u32, P, P, szt, P]
         L.zero1_mta_step.restype = i32
+        L.zero1_mta_step_static.argtypes = [P, i32, i64, ctypes.POINTER(Plan), ctypes.POINTER(HParams),
+                                            P, i32, i32, u32, P, P]
+        L.zero1_mta_step_static.restype = i32
         L.zero1_step_scalars_derive.argtypes = [ctypes.POINTER(HParams), ctypes.POINTER(StepScalars)]
         L.zero1_step_scalars_derive.restype = i32
         L.zero1_arena_plan.argtypes = [ctypes.POINTER(ArenaRequest), ctypes.POINTER(ArenaLayout)]
@@ -342,6 +346,16 @@ def mta_step(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, my_ran
     _check(lib().zero1_mta_step(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
                                 ctypes.byref(h), _addr(rank_sumsq), n_ranks, my_rank, flags,
                                 _addr(info_out), w, wb, _stream(stream)))
+
+
+def mta_step_static(grads, begin: int, plan: Plan, hp, rank_sumsq, n_ranks: int, my_rank: int,
+                    flags: int = 0, info_out=None, stream=None):
+    """zero1_mta_step with the workspace in the library's static device array."""
+    arr = _ptrs(grads)
+    h = _hp(hp)
+    _check(lib().zero1_mta_step_static(ctypes.cast(arr, P), len(grads), begin, ctypes.byref(plan),
+                                       ctypes.byref(h), _addr(rank_sumsq), n_ranks, my_rank, flags,
+                                       _addr(info_out), _stream(stream)))
 
 
 def arena_plan(shard_len: int, W: int, grad_elems: int, grad_offset: int, param_elems: int,

@@ -14,7 +14,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzero1.so")
-SOURCES = [os.path.join(HERE, "csrc", "api.cpp"), os.path.join(HERE, "csrc", "kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "api.cpp"), os.path.join(HERE, "csrc", "kernels.hip"),
+           os.path.join(HERE, "csrc", "static_ws.hip")]
 # bandwidth calibration kernels used by bench.py (not part of the step library)
 CALIB_LIB = os.path.join(HERE, "libzero1_calib.so")
 CALIB_SOURCES = [os.path.join(HERE, "csrc", "calib.hip")]

@@ -112,9 +112,6 @@ zero1_status current_device(DevInfo& out)
 }
 
 // ------------------------------------------------------------------ layout
-constexpr size_t kInfoBytes = 256;
-constexpr size_t kPartialBytes = sizeof(double) * kMaxPartials;
-constexpr size_t kGOffset = kInfoBytes + kPartialBytes;   // multiple of 256
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -302,6 +299,12 @@ struct LaunchRequestScope {
 };
 
 }  // namespace
+
+int z1::set_error(int st, const char* msg)
+{
+    g_last_error = msg;
+    return st;
+}
 
 // ====================================================================== ABI
 extern "C" {

@@ -28,6 +28,12 @@ constexpr int kChunkElems = 2048;   // multi-tensor chunk: one tile
 #ifndef Z1_G_NT_BYTES
 #define Z1_G_NT_BYTES (128ll << 20) // g larger than this is stored non-temporally
 #endif
+// Workspace layout (zero1_workspace_bytes): the norm info, the per-workgroup
+// fp64 partials, then the fp32 g of the store-g design.
+constexpr size_t kInfoBytes = 256;
+constexpr size_t kPartialBytes = sizeof(double) * kMaxPartials;
+constexpr size_t kGOffset = kInfoBytes + kPartialBytes;   // multiple of 256
+
 constexpr int kReducePerCu = Z1_REDUCE_PER_CU;
 constexpr int kUpdatePerCu = Z1_UPDATE_PER_CU;
 constexpr long long kGNtBytes = Z1_G_NT_BYTES;
@@ -88,6 +94,10 @@ struct ChunkDesc {
     int32_t len;
     int64_t offset;   // element offset inside the piece
 };
+
+// ---- error state of the calling thread (zero1_last_error): records the
+// message and returns st (a zero1_status).
+int set_error(int st, const char* msg);
 
 // ---- timing request for the next launch on the calling thread
 // (zero1_time_next_launch): the next kernel the launchers below start takes
