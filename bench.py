@@ -43,6 +43,7 @@ from __future__ import annotations
 import argparse
 import csv
 import ctypes
+import gc
 import glob
 import hashlib
 import json
@@ -371,12 +372,17 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     per_copy = cfg.S * (2 * W + 26 + (4 if store_g else 0))
     n_copies = 2 if per_copy < (1 << 30) else 1
     design = z.STORE_G if store_g else z.RECOMPUTE_G
+    gc.collect()
     st = setup(torch, cfg, design, n_copies, dev, layout)
     S = st["S"]
     c0 = st["copies"][0]
     assert z.mta_design(c0.grads, c0.begin, c0.plan, 0) == design
     run_steps(z, cfg, st, design, 0, warmup)
     torch.cuda.synchronize()
+    # no garbage collection inside the timed passes: a full collection (tens
+    # of ms with torch loaded) would land in the middle of a step
+    gc.collect()
+    gc.disable()
     # the timed region: exactly K steps back to back, bracketed by synchronizations
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -399,6 +405,7 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     torch.cuda.synchronize()
     run_steps(z, cfg, st, design, warmup + steps, warmup + 2 * steps, events)
     torch.cuda.synchronize()
+    gc.enable()
     upd_ms = statistics.fmean(e[1][0].elapsed_time(e[1][1]) for e in events)
     red_ms = statistics.fmean(e[0][0].elapsed_time(e[0][1]) for e in events)
     ms = el * 1e3 / steps
@@ -446,6 +453,7 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
             kk["ceiling_tiles_in_flight"] = cal[k]["tiles_in_flight"]
         res["ceiling_ms_per_step"] = cal["step_shard_ms"]
     del st, c0
+    gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
