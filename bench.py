@@ -103,13 +103,13 @@ def cal_lib():
             raise ImportError(f"{path} is not built: run __graft_entry__.build()")
         L = ctypes.CDLL(path)
         P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
-        L.zcal_stream.argtypes = [P, P, P, i32, P, P, P, i32, i64, i32, i32, i32, i32, P, P]
+        L.zcal_stream.argtypes = [P, P, P, i32, P, P, P, i32, i64, i32, i32, i32, i32, i32, P, P]
         L.zcal_stream.restype = i32
         _cal = L
     return _cal
 
 
-def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream, tiles_in_flight=1, wide=0):
+def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream, tiles_in_flight=1, wide=0, contig=0):
     """One calibration pass.  rd: [(device address, bytes per element, plain
     loads?)]; wr: [(device address, bytes per element, sc1 stores?)]; every
     stream must hold n_tiles * 2048 elements from its address."""
@@ -122,7 +122,7 @@ def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream, tiles_in_flight=1, w
                                arr(ctypes.c_int, [int(x[2]) for x in rd]), R,
                                arr(ctypes.c_void_p, [x[0] for x in wr]), arr(ctypes.c_int, [x[1] for x in wr]),
                                arr(ctypes.c_int, [int(x[2]) for x in wr]), Wn,
-                               n_tiles, tiles_in_flight, wide, grid, split, sink, stream)
+                               n_tiles, tiles_in_flight, wide, contig, grid, split, sink, stream)
     if st != 0:
         raise RuntimeError(f"zcal_stream failed with status {st}")
 

@@ -52,6 +52,7 @@ struct Streams {
     uint8_t wr_sc1[kMaxWr];     // 1: sc1 buffer stores, 0: non-temporal
     int n_rd, n_wr;
     int wide;                   // lane layout: 0 two quads, 1 eight consecutive elements
+    int contig;                 // 1: the U tiles taken together are consecutive tiles
 };
 
 template <typename T>
@@ -133,8 +134,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Streams s, int64_t nti
     const int64_t x = b % nx, per = (ntiles + nx - 1) / nx;
     const int64_t lo = x * per, hi = lo + per < ntiles ? lo + per : ntiles;
     const int64_t step = G / nx;
+    // tile j of a group: t + j * jstep; groups advance by gstep
+    const int64_t jstep = s.contig ? 1 : step;
+    const int64_t t0 = s.contig ? lo + (b / nx) * U : lo + b / nx;
+    const int64_t gstep = U * step;
     u32x4 tot = {0u, 0u, 0u, 0u};
-    for (int64_t t = lo + b / nx; t < hi; t += U * step) {
+    for (int64_t t = t0; t < hi; t += gstep) {
         u32x4 acc[U][2];
 #pragma unroll
         for (int j = 0; j < U; ++j) acc[j][0] = acc[j][1] = u32x4{0u, 0u, 0u, 0u};
@@ -145,9 +150,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Streams s, int64_t nti
 #pragma unroll
                 for (int k = 0; k < B; ++k) {
                     part[j][k][0] = part[j][k][1] = u32x4{0u, 0u, 0u, 0u};
-                    if (k0 + k < s.n_rd && t + j * step < hi)
+                    if (k0 + k < s.n_rd && t + j * jstep < hi)
                         ld_fold(s.rd[k0 + k], s.rd_bytes[k0 + k], s.rd_plain[k0 + k], s.wide,
-                                (t + j * step) * kTile, part[j][k]);
+                                (t + j * jstep) * kTile, part[j][k]);
                 }
             }
 #pragma unroll
@@ -161,9 +166,9 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Streams s, int64_t nti
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            if (t + j * step < hi) {
+            if (t + j * jstep < hi) {
                 for (int k = 0; k < s.n_wr; ++k)
-                    st_acc(s.wr[k], s.wr_bytes[k], s.wr_sc1[k], s.wide, (t + j * step) * kTile, acc[j],
+                    st_acc(s.wr[k], s.wr_bytes[k], s.wr_sc1[k], s.wide, (t + j * jstep) * kTile, acc[j],
                            (uint32_t)k);
                 tot ^= acc[j][0] ^ acc[j][1];
             }
@@ -190,6 +195,9 @@ extern "C" {
 //   tiles_in_flight: U in {1, 2, 4, 8} (tiles whose loads are issued together).
 //   wide: 0 for the step kernels' lane layout (two quads 256 elements apart),
 //     1 for eight consecutive elements per lane.
+//   contig: 0 -- the U tiles a workgroup takes together are its next U tiles
+//     in the walk (one stride apart); 1 -- they are U consecutive tiles (the
+//     workgroup reads U * 2048 contiguous elements of each stream at once).
 //   grid, split: workgroups, and 8 (one contiguous part of the tiles per XCD;
 //     grid a multiple of 8) or 1 (a plain grid stride).
 //   sink: grid uint32 words of device memory (written only in a case that
@@ -198,7 +206,7 @@ extern "C" {
 // Returns 0, 1 for a bad argument, or 2 + the HIP error code of the launch.
 int zcal_stream(const void* const* rd, const int* rd_bytes, const int* rd_plain, int n_rd, void* const* wr,
                 const int* wr_bytes, const int* wr_sc1, int n_wr, int64_t n_tiles, int tiles_in_flight,
-                int wide, int grid, int split, void* sink, void* stream)
+                int wide, int contig, int grid, int split, void* sink, void* stream)
 {
     if (n_rd < 0 || n_rd > kMaxRd || n_wr < 0 || n_wr > kMaxWr || n_tiles < 0 || grid < 1 || !sink ||
         (split != 1 && split != 8))
@@ -220,6 +228,7 @@ int zcal_stream(const void* const* rd, const int* rd_bytes, const int* rd_plain,
     s.n_rd = n_rd;
     s.n_wr = n_wr;
     s.wide = wide ? 1 : 0;
+    s.contig = contig ? 1 : 0;
     if (n_tiles == 0) return 0;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     uint32_t* sk = static_cast<uint32_t*>(sink);
