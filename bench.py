@@ -670,7 +670,8 @@ def calibrate(torch, dev, gib=4, spacing_gib=40):
     kernels: the store-g update (g, master, m, v read; master, m, v written in
     place; bf16 parameters written) and the 8-slice reduce (8 bf16 slices
     read, fp32 g written; spaced: g in the first slot, the slices packed from
-    the fifth, as the arena places them).  Returns a dict of GB/s."""
+    the fifth, as the arena places them).  Then the update mix at a range of
+    spacings (spacing_sweep).  Returns a dict of GB/s."""
     n = (gib << 30) // 4 // 2048 * 2048          # elements per buffer
     n_tiles = n // 2048
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -719,7 +720,32 @@ def calibrate(torch, dev, gib=4, spacing_gib=40):
             arena = None
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
+    out["update_mix_by_spacing_GBps"] = spacing_sweep(torch, dev, sink, stream, cus)
     return out
+
+
+def spacing_sweep(torch, dev, sink, stream, cus, spacings_gib=(1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48)):
+    """The update mix (g, master, m, v read; master, m, v rewritten; bf16
+    written) over 1 GiB fp32 streams placed D GiB apart in one allocation, for
+    each D: {D: GB/s}."""
+    n = (1 << 30) // 4 // 2048 * 2048
+    n_tiles = n // 2048
+    dmax = max(spacings_gib) << 30
+    arena = torch.empty(4 * dmax + 2 * n, dtype=torch.uint8, device=dev)
+    arena.fill_(0x3c)
+    base = arena.data_ptr()
+    res = {}
+    for D in spacings_gib:
+        o = [k * (D << 30) for k in range(5)]
+        rd = [(base + o[k], 4, False) for k in range(4)]
+        wr = [(base + o[k], 4, False) for k in (1, 2, 3)] + [(base + o[4], 2, False)]
+        ms, _ = best_calibration(torch, rd, wr, n_tiles, 8 * cus, 8, sink.data_ptr(), stream, reps=5)
+        res[D] = n_tiles * 2048 * 30 / (ms * 1e-3) / 1e9
+        log(f"calibrate update mix, streams {D} GiB apart: {res[D]:.0f} GB/s")
+    del arena
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------------- main
