@@ -22,8 +22,8 @@ step in one allocation laid out by zero1_arena_plan: the update's five streams
 
 Per kernel the line gives the algorithmic bytes over its own duration (HIP
 events stamped by the kernel's dispatch), the bytes the design moves, and a
-calibrated ceiling: the time of a kernel that moves exactly the same streams
-with the same access pattern and placement and computes nothing
+same-traffic calibration: the time of a kernel that moves exactly the same
+streams with the same access pattern and placement and computes nothing
 (libzero1_calib.so).
 
 Prints ONE JSON line.  Metric: shard parameters updated per second; the
@@ -313,11 +313,13 @@ def run_steps(z, cfg, st, flags, k0, k1, events=None):
             z.mta_update(c.grads, c.begin, c.plan, h, c.rsd, W, flags=flags, ws=c.ws)
 
 
-def ceilings(torch, z, cfg, st, store_g, cus):
-    """Calibrated ceilings of the two kernels of the step: the same streams
-    (copy 0's arrays, at their addresses), moved with the same access pattern
-    and launch shape by a kernel that computes nothing.  Run after the timed
-    passes (it overwrites the arrays)."""
+def calibrated(torch, z, cfg, st, store_g, cus):
+    """Same-traffic calibration of the two kernels of the step: the same
+    streams (copy 0's arrays, at their addresses), moved with the same access
+    pattern and launch shape by a kernel that computes nothing -- what HBM
+    delivers for that traffic, a reference for the step kernels (which run a
+    little faster than this generic kernel).  Run after the timed passes (it
+    overwrites the arrays)."""
     W, S = st["W"], st["S"]
     c = st["copies"][0]
     mvb = 2 if cfg.mv_bf16 else 4
@@ -366,7 +368,7 @@ def ceilings(torch, z, cfg, st, store_g, cus):
 
 def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     """One workload in one layout: warmup, K timed steps, K kernel-timed steps,
-    the calibrated ceilings (and, for the store-g design, the bucketed flow)."""
+    the same-traffic calibration (and, for the store-g design, the bucketed flow)."""
     W = cfg.W
     store_g = W > 4
     per_copy = cfg.S * (2 * W + 26 + (4 if store_g else 0))
@@ -443,15 +445,15 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     if bucketed and store_g:
         res["bucketed"] = bucketed_timing(torch, z, cfg, st, warmup + 2 * steps, min(steps, 50))
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    cal = ceilings(torch, z, cfg, st, store_g, cus)
+    cal = calibrated(torch, z, cfg, st, store_g, cus)
     if cal:
         for k in ("reduce", "update"):
             kk = res["kernels"][k]
-            kk["ceiling_ms"] = cal[k]["shard_ms"]
-            kk["ceiling_moved_GBps"] = cal[k]["GBps"]
-            kk["frac_of_ceiling"] = cal[k]["shard_ms"] / kk["ms"]
-            kk["ceiling_tiles_in_flight"] = cal[k]["tiles_in_flight"]
-        res["ceiling_ms_per_step"] = cal["step_shard_ms"]
+            kk["calibrated_ms"] = cal[k]["shard_ms"]
+            kk["calibrated_moved_GBps"] = cal[k]["GBps"]
+            kk["calibrated_over_kernel"] = cal[k]["shard_ms"] / kk["ms"]
+            kk["calibrated_tiles_in_flight"] = cal[k]["tiles_in_flight"]
+        res["calibrated_ms_per_step"] = cal["step_shard_ms"]
     del st, c0
     gc.collect()
     torch.cuda.synchronize()
@@ -845,10 +847,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": UPDATE_KERNEL, "achieved": upd["algorithmic_GBps"],
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": upd["algorithmic_GBps"] / PEAK_HBM_GBS,
                      "traffic": upd["traffic"], "algorithmic_bytes_per_launch": upd["algorithmic_bytes"],
-                     "kernel_ms": upd["ms"], "ceiling_ms": upd.get("ceiling_ms"),
-                     "frac_of_ceiling": upd.get("frac_of_ceiling")},
+                     "kernel_ms": upd["ms"], "calibrated_ms": upd.get("calibrated_ms"),
+                     "calibrated_over_kernel": upd.get("calibrated_over_kernel")},
         "kernels": h["kernels"],
-        "ceiling_ms_per_step": h.get("ceiling_ms_per_step"),
+        "calibrated_ms_per_step": h.get("calibrated_ms_per_step"),
         "layouts": {lay: {k: head[lay][k] for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout")}
                     for lay in layouts},
     }

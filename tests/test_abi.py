@@ -329,7 +329,7 @@ def test_bench_entry_points_and_gpu_count_contract():
     import subprocess
     import sys
     import bench
-    for name in ("setup", "run_steps", "measure", "ceilings", "calibrate", "cpu_baseline", "bucketed_timing",
+    for name in ("setup", "run_steps", "measure", "calibrated", "calibrate", "cpu_baseline", "bucketed_timing",
                  "summarize_pmc", "summarize_kt", "traffic_from_summary", "kernel_source_hash", "main"):
         assert callable(getattr(bench, name)), name
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
