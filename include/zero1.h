@@ -397,11 +397,12 @@ zero1_status zero1_time_next_launch(void* start_event, void* stop_event);
  * arena).  On MI355X the HBM throughput of a kernel that streams several
  * arrays at once depends on how far apart the arrays are: the update's five
  * streams (the reduced gradient g -- or gradient slice 0 when g is recomputed
- * --, master, m, v and the shard's bf16 parameters) run at about 6.2 TB/s when
- * they are far apart and at about 5.1 TB/s when packed within 12 GiB
- * (Llama-7B/8 shard; 6.7 vs 6.2 TB/s at the GPT-2-small/8 shard), and the
- * W-slice reduce is faster when the slices sit well away from g (7.5e9/64
- * shard: 2.40 vs 2.90 ms).  The planner puts those five at one spacing D
+ * --, master, m, v and the shard's bf16 parameters) move 5.7-5.8 TB/s when
+ * they are 24 GiB or more apart and 4.5-5.0 TB/s when they are 12 GiB or
+ * less apart (1 GiB streams, a kernel that only moves them); on the step, the
+ * Llama-7B/8 shard's update moves 6.2 TB/s in the arena against 5.3 TB/s with
+ * one allocation per array, and the whole 7e9-parameter W=1 step takes
+ * 34.0 ms against 39.7.  The planner puts those five at one spacing D
  * (40 GiB, or more when an array is larger, or less when `capacity` is short)
  * and packs the remaining gradient buffers after the parameter buffer.  The
  * gaps between the spaced arrays are not used by the library: the caller may
