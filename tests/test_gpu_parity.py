@@ -1319,3 +1319,48 @@ def test_host_threads_step_ranks_concurrently(env):
         assert_f32_equal(m, o.m, f"m rank {r}")
         assert_f32_equal(v, o.v, f"v rank {r}")
         assert_bf16_equal(p, o.param, f"param rank {r}")
+
+
+def test_empty_shard_rank(env):
+    """A rank whose shard is empty (N = 10 cut into W = 8 shards of 2: ranks 5-7
+    own nothing) still takes part in the step: its reduce writes a partial of
+    0, its update writes the global norm and clip decision formed from every
+    rank's partial and touches no element, an empty bucket's partial is 0, and
+    an empty partials sum is 0."""
+    torch, dev = env
+    N, W = 10, 8
+    G = replicas(0xE5, 1, W, N, 0.7)
+    gd = [to_dev_u16(torch, g, dev) for g in G]
+    parts = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                      for b, n in (z.shard_range(N, W, r) for r in range(W))])
+    assert [z.shard_range(N, W, r)[1] for r in range(W)] == [2, 2, 2, 2, 2, 0, 0, 0]
+    ws = ws_tensor(torch, z.workspace_bytes(0, W), dev)
+    rsd = torch.from_numpy(parts.copy()).to(dev)
+    rsd[6] = 123.0
+    b6, n6 = z.shard_range(N, W, 6)
+    z.shard_reduce(gd, b6, n6, sumsq_out=rsd[6:7], ws=ws)
+    info = torch.full((4,), -1.0, dtype=torch.float64, device=dev)
+    sentinel = torch.full((8,), 7.0, dtype=torch.float32, device=dev)
+    p16 = torch.full((8,), 0x1234, dtype=torch.int16, device=dev)
+    z.adamw_step(None, gd, b6, 0, sentinel, sentinel[2:], sentinel[4:], p16, hp_at(1), rsd, W, info_out=info)
+    one = torch.full((1,), 5.0, dtype=torch.float64, device=dev)
+    z.partials_sum(one, 0, one)
+    torch.cuda.synchronize()
+    assert rsd[6].item() == 0.0
+    norm = oracle.global_norm(parts)
+    clip, coef = oracle.clip_coef(norm, 1.0)
+    ni = info.cpu().numpy()
+    assert rel_close(ni[0], float(parts.sum()), NORM_TOL) and rel_close(ni[1], norm, NORM_TOL)
+    assert bool(ni[2:4].view(np.int32)[1]) == clip and ni[2:3].view(np.float32)[0] == (coef if clip else 1.0)
+    assert (sentinel.cpu().numpy() == 7.0).all() and (to_np_u16(p16) == 0x1234).all()
+    assert one.item() == 0.0
+    # an empty bucket of a real plan: its partial is 0 and it writes nothing
+    numels = [4096]
+    master_full = synth.f32(4096, synth.master_key(3), 0, 0.02)
+    a = MtaShard(torch, dev, numels, 1, 0, master_full)
+    wsg = a.workspace(z.STORE_G)
+    part = torch.full((1,), 9.0, dtype=torch.float64, device=dev)
+    g1 = [to_dev_u16(torch, synth.bf16(4096, 11, 0, 0.1), dev)]
+    z.mta_reduce_range([g1[0].data_ptr() + 2 * 100], a.plan, 100, 100, part, ws=wsg)
+    torch.cuda.synchronize()
+    assert part.item() == 0.0
