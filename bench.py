@@ -444,6 +444,11 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
         kk["traffic"] = traffic_from_summary(pmc_summary_path(cfg.name), k) if layout == "arena" else None
     if bucketed and store_g:
         res["bucketed"] = bucketed_timing(torch, z, cfg, st, warmup + 2 * steps, min(steps, 50))
+    if ms < 0.2:   # launch-bound sizes: the same step replayed from a captured graph
+        gc.collect()
+        gc.disable()
+        res["graph"] = graph_timing(torch, z, cfg, st, design, warmup + 2 * steps + 100)
+        gc.enable()
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     cal = calibrated(torch, z, cfg, st, store_g, cus)
     if cal:
@@ -610,6 +615,52 @@ def traffic_from_summary(path, kernel):
         return float(kv[f"{kernel}_fetch_bytes"]) + float(kv[f"{kernel}_write_bytes"])
     except (KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------------- graph replay
+def graph_timing(torch, z, cfg, st, design, k0, replays=40, per_graph=10):
+    """The launch-bound path: per_graph consecutive steps captured once into
+    one HIP graph (torch.cuda.graph), each step reading its fp32 scalars
+    (t, learning rate) from its own 40-byte slot of device memory
+    (zero1_hparams.device_scalars); before every replay the next per_graph
+    steps' scalars are derived on the host and copied in (one stream-ordered
+    copy from pinned memory, inside the timed region).  Returns ms per step."""
+    W, rank = st["W"], st["rank"]
+    copies = st["copies"]
+    dev = copies[0].master.device
+    slot = 40
+    dev_scal = torch.zeros(per_graph * slot // 8, dtype=torch.float64, device=dev)
+    host = torch.zeros(per_graph * slot, dtype=torch.uint8).pin_memory()
+    base = dev_scal.data_ptr()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(per_graph):
+            c = copies[j % len(copies)]
+            z.mta_step(c.grads, c.begin, c.plan, {"device_scalars": base + slot * j}, c.rsd, W, rank,
+                       flags=design, ws=c.ws)
+    torch.cuda.synchronize()
+
+    def fill(t0):
+        buf = bytearray()
+        for j in range(per_graph):
+            buf += bytes(z.step_scalars_derive(cfg.hparams(t0 + j)))
+        host.copy_(torch.frombuffer(buf, dtype=torch.uint8))
+        dev_scal.view(torch.uint8).copy_(host, non_blocking=True)
+
+    fill(k0 + 1)
+    graph.replay()
+    torch.cuda.synchronize()
+    t = k0 + 1 + per_graph
+    t_start = time.perf_counter()
+    for _ in range(replays):
+        fill(t)
+        graph.replay()
+        t += per_graph
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t_start) * 1e3 / (replays * per_graph)
+    del graph
+    return {"steps_per_graph": per_graph, "replays": replays, "ms_per_step": ms}
 
 
 # ---------------------------------------------------------------------- bucketed flow
@@ -854,8 +905,9 @@ def main():
         "layouts": {lay: {k: head[lay][k] for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout")}
                     for lay in layouts},
     }
-    if "bucketed" in h:
-        out["bucketed"] = h["bucketed"]
+    for extra in ("bucketed", "graph"):
+        if extra in h:
+            out[extra] = h[extra]
     if not a.no_per_config:
         per = {}
         for name in PER_CONFIG:
