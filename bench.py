@@ -371,8 +371,11 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     the same-traffic calibration (and, for the store-g design, the bucketed flow)."""
     W = cfg.W
     store_g = W > 4
+    # copies rotated so that a step never finds the previous steps' data in
+    # the 256 MB MALL: at least 512 MiB of other traffic between two uses of
+    # one copy (bytes a step touches per copy: the design's byte count)
     per_copy = cfg.S * (2 * W + 26 + (4 if store_g else 0))
-    n_copies = 2 if per_copy < (1 << 30) else 1
+    n_copies = 1 if per_copy >= (1 << 30) else min(64, max(2, -(-(512 << 20) // per_copy) + 1))
     design = z.STORE_G if store_g else z.RECOMPUTE_G
     gc.collect()
     st = setup(torch, cfg, design, n_copies, dev, layout)
