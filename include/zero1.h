@@ -379,7 +379,7 @@ zero1_status zero1_mta_step_static(const uint16_t* const* grads, int W, int64_t 
  * from that kernel's own dispatch (hipExtLaunchKernel), with no marker packets
  * around it, so hipEventElapsedTime(start, stop) is the kernel's duration as a
  * kernel trace reports it.  Which kernel is first: the reduce of the reduce
- * calls and of the two-phase zero1_mta_step, the update of zero1_adamw_step
+ * calls and of zero1_mta_step, the update of zero1_adamw_step
  * and zero1_mta_update, the sum of squares of zero1_grad_norm, the partials
  * sum of zero1_partials_sum (and of an empty zero1_shard_reduce /
  * zero1_grad_norm).  The request is dropped when that call returns, whether

@@ -244,7 +244,7 @@ def test_gpt2_small_w8_full_shards(env):
             assert rel_close(ni[1], oi.norm, NORM_TOL)
             assert bool(ni[2:4].view(np.int32)[1]) == oi.clip and oi.clip
             assert ni[2:3].view(np.float32)[0] == oi.coef
-        log(f"[C2] step {t}: norm {oi.norm:.6g} coef {float(oi.coef):.6g} ({time.time() - ts:.1f}s)")
+        log(f"[GPT-2 small W=8] step {t}: norm {oi.norm:.6g} coef {float(oi.coef):.6g} ({time.time() - ts:.1f}s)")
     for r in range(W):
         sh = shards[r]
         idx = np.arange(sh.S, dtype=np.int64)

@@ -394,8 +394,8 @@ def test_mta_misaligned_pieces(env):
 
 @pytest.mark.parametrize("design", [0, z.STORE_G, z.RECOMPUTE_G])
 def test_c1_full_trajectory(env, design):
-    """C1: flat 2^20 parameters, W=4, every rank, 10 steps, against the oracle
-    (design 0: the library's choice, the single-launch on-chip step)."""
+    """The flat 2^20-parameter model at W=4, every rank, 10 steps, against the
+    oracle (design 0: the library's choice, recompute at W = 4)."""
     from synth.workloads import configs
     c = configs()["C1"]
     torch, dev = env
