@@ -49,6 +49,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -474,11 +475,37 @@ CPU_SAMPLE = {"C1": None, "C2": None, "C3": 1 << 20, "C4": 1 << 22, "C5a": 1 << 
 
 
 def cpu_model():
+    """The host CPU as lscpu describes it: model name, family / model /
+    stepping, sockets x cores x threads, L3 size, hypervisor (a virtual
+    machine may report only a generic model name)."""
+    fields = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "unknown")
-    except OSError:
-        return "unknown"
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    name = fields.get("Model name")
+    if not name:
+        try:
+            with open("/proc/cpuinfo") as f:
+                name = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "unknown")
+        except OSError:
+            name = "unknown"
+    parts = [name]
+    if "CPU family" in fields:
+        parts.append(f"family {fields['CPU family']} model {fields.get('Model', '?')} "
+                     f"stepping {fields.get('Stepping', '?')}")
+    if "Socket(s)" in fields:
+        parts.append(f"{fields['Socket(s)']} socket(s) x {fields.get('Core(s) per socket', '?')} cores x "
+                     f"{fields.get('Thread(s) per core', '?')} threads")
+    if "L3 cache" in fields:
+        parts.append(f"L3 {fields['L3 cache']}")
+    if "Hypervisor vendor" in fields:
+        parts.append(f"virtual machine ({fields['Hypervisor vendor']})")
+    return "; ".join(parts)
 
 
 def cpu_baseline(cfg, budget_s=2.0, max_steps=2000):
