@@ -354,7 +354,11 @@ zero1_status zero1_mta_step(const uint16_t* const* grads, int W, int64_t begin,
  *     rejected with ZERO1_EINVAL before anything is launched; with
  *     ZERO1_RECOMPUTE_G any shard length fits.
  *   - The array's device address is looked up once per device, on the first
- *     call with that device current; the call allocates nothing.
+ *     call with that device current.  That first lookup is when the HIP
+ *     runtime loads the code object holding the array onto the device (and
+ *     maps its memory); later calls allocate nothing and only launch
+ *     kernels, so a caller that captures the step into a graph makes one call
+ *     on each device before capturing.
  *   - Each call writes every byte of the array it reads before reading it,
  *     so nothing needs to start at zero.  All calls on one GPU share its
  *     array: calls that overlap in time on one GPU (different streams, or
