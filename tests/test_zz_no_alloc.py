@@ -65,3 +65,49 @@ def test_static_step_matches_workspace_step(W, design):
         assert_bf16_equal(gb[3], ga[3], f"param static vs workspace, {what}")
         assert b.untouched_outside(), what
         assert np.isfinite(gb[0]).all()
+
+
+@pytest.mark.gpu
+def test_static_step_replays_from_a_captured_graph():
+    """The use the entry point is for: after one eager call on the device,
+    the step is captured into a HIP graph without a workspace and replayed
+    three times, with eager work between the replays; each replay equals a
+    zero1_mta_step call with a caller's workspace, bit for bit."""
+    from tests.gpu_util import torch_cuda
+    torch = torch_cuda()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W, rank = 8, 5
+    numels = [300_001, 7, 2_048 * 50 + 9, 90_000]
+    N = sum(numels)
+    master_full = synth.f32(N, synth.master_key(0x6A9), 0, 0.02)
+    a = MtaShard(torch, dev, numels, W, rank, master_full)
+    b = MtaShard(torch, dev, numels, W, rank, master_full)
+    G = [synth.bf16(N, synth.grad_key(0x6A9, 1, w), 0, 0.02, 1) for w in range(W)]
+    gd = [to_dev_u16(torch, x, dev) for x in G]
+    rs_a = torch.full((W,), 0.3, dtype=torch.float64, device=dev)
+    rs_b = rs_a.clone()
+    ia = torch.zeros(4, dtype=torch.float64, device=dev)
+    ib = torch.zeros(4, dtype=torch.float64, device=dev)
+    ws = a.workspace()
+    # the eager first call on this device (looks the array up)
+    z.mta_step(gd, a.begin, a.plan, hp_at(1), rs_a, W, rank, info_out=ia, ws=ws)
+    z.mta_step_static(gd, b.begin, b.plan, hp_at(1), rs_b, W, rank, info_out=ib)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        z.mta_step_static(gd, b.begin, b.plan, hp_at(2), rs_b, W, rank, info_out=ib)
+    torch.cuda.synchronize()
+    scratch = torch.ones(1 << 20, device=dev)
+    for k in range(3):
+        z.mta_step(gd, a.begin, a.plan, hp_at(2), rs_a, W, rank, info_out=ia, ws=ws)
+        graph.replay()
+        scratch.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        ga, gb = a.gather(), b.gather()
+        for j, name in ((0, "master"), (1, "m"), (2, "v")):
+            assert_f32_equal(gb[j], ga[j], f"{name} replay {k}")
+        assert_bf16_equal(gb[3], ga[3], f"param replay {k}")
+        assert ia.cpu().numpy().tobytes() == ib.cpu().numpy().tobytes()
+        assert rs_a.cpu().numpy().tobytes() == rs_b.cpu().numpy().tobytes()
+    del graph
