@@ -448,6 +448,10 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
         kk["traffic"] = traffic_from_summary(pmc_summary_path(cfg.name), k) if layout == "arena" else None
     if bucketed and store_g:
         res["bucketed"] = bucketed_timing(torch, z, cfg, st, warmup + 2 * steps, min(steps, 50))
+        gc.collect()
+        gc.disable()
+        res["bucketed"]["with_backward_gemms"] = bucketed_overlap(torch, z, cfg, st, warmup + 2 * steps + 60)
+        gc.enable()
     if ms < 0.2:   # launch-bound sizes: the same step replayed from a captured graph
         gc.collect()
         gc.disable()
@@ -741,6 +745,60 @@ def bucketed_timing(torch, z, cfg, st, k0, steps, bucket_bytes=25_000_000):
         crit_ms.append(ev[2 * nb - 1].elapsed_time(ev[2 * nb]))
     return dict(bucket_params=b, buckets=nb, reduce_ms=sum(red_ms) / steps,
                 after_backward_ms=sum(crit_ms) / steps)
+
+
+def bucketed_overlap(torch, z, cfg, st, k0, steps=20, bucket_bytes=25_000_000):
+    """The point of the bucketed flow: the bucket reduces run while backward
+    still computes.  Backward is stood in for by one bf16 GEMM per bucket (a
+    layer's weight-gradient product, 8192 tokens x 768 x 3072 on the main
+    stream); each bucket's reduce is issued on a second stream once its GEMM
+    has finished (an event), as a ZeRO-2 engine issues it.  Per step (ms): the
+    GEMMs alone, GEMMs and bucket reduces one after the other on one stream,
+    and the two streams overlapped (to the end of the last reduce), each
+    followed by nothing else (the partials sum and the update after backward
+    are timed by bucketed_timing)."""
+    W, rank, S = st["W"], st["rank"], st["S"]
+    b = max(2048, bucket_bytes // (2 * W) // 2048 * 2048)
+    ranges = [(lo, min(S, lo + b)) for lo in range(0, S, b)][::-1]
+    nb = len(ranges)
+    dev = st["copies"][0].master.device
+    x = torch.randn(8192, 768, dtype=torch.bfloat16, device=dev).t().contiguous()   # 768 x 8192
+    dy = torch.randn(8192, 3072, dtype=torch.bfloat16, device=dev)                   # 8192 x 3072
+    dw = torch.empty(768, 3072, dtype=torch.bfloat16, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev)        # default priority
+    done = [torch.cuda.Event() for _ in range(nb)]
+
+    def buckets(c, stream):
+        for i, (lo, hi) in enumerate(ranges):
+            yield i, lambda lo=lo, hi=hi, i=i: z.mta_reduce_range(
+                [g.data_ptr() + 2 * (c.begin + lo) for g in c.grads], c.plan, lo, hi,
+                c.parts.data_ptr() + 8 * (nb - 1 - i), flags=z.STORE_G, ws=c.ws, stream=stream.cuda_stream)
+
+    def one(k, mode):
+        c = st["copies"][k % len(st["copies"])]
+        if not hasattr(c, "parts"):
+            c.parts = torch.zeros(nb, dtype=torch.float64, device=dev)
+        for i, call in buckets(c, side if mode == "overlap" else main):
+            torch.mm(x, dy, out=dw)
+            if mode == "gemm":
+                continue
+            if mode == "overlap":
+                done[i].record(main)
+                side.wait_event(done[i])
+            call()
+
+    out = {"bucket_params": b, "buckets": nb, "gemm": "bf16 768x8192 @ 8192x3072 per bucket"}
+    for mode in ("gemm", "sequential", "overlap"):
+        one(k0, mode)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(k0, k0 + steps):
+            one(k, mode)
+        torch.cuda.synchronize()
+        out[f"{mode}_ms"] = (time.perf_counter() - t0) * 1e3 / steps
+    del x, dy, dw
+    return out
 
 
 # ---------------------------------------------------------------------- calibrate mode
