@@ -347,7 +347,9 @@ def calibrated(torch, z, cfg, st, store_g, cus):
         upd_rd = [(a, 2, False) for a in grads] + state_rd
     sink = torch.zeros(8192, dtype=torch.int32, device=c.master.device)
     stream = torch.cuda.current_stream().cuda_stream
-    rg, rs = launch_shape(n_tiles, cus, 8, lambda u, n: u >= 16 * n)
+    # the library's reduce grid: 8 workgroups per CU, 6 for the sum-of-squares
+    # pass over one to four slices (its few-slice kernel)
+    rg, rs = launch_shape(n_tiles, cus, 8 if store_g else 6, lambda u, n: u >= 16 * n)
     ug, us = launch_shape(n_tiles, cus, 8 if n_tiles > 8192 else 0, lambda u, n: u > 8192)
     out = {}
     passes = (("reduce", red_rd, red_wr, rg, rs), ("update", upd_rd, state_wr, ug, us))

@@ -1,9 +1,10 @@
 """GPU parity at the sizes where the kernels change shape, against the CPU oracle.
 
 The launch shape of each pass depends on the number of 2048-element tiles:
-  * the sum-of-squares pass of the recompute design (W <= 4) loads U = 8/W
-    tiles together (4 for W = 3) once a workgroup owns at least U tiles, i.e.
-    once the shard has more tiles than U times the 2048-workgroup grid;
+  * the sum-of-squares pass of the recompute design (W <= 4) runs on a grid
+    of 6 workgroups per CU (1536) and loads U tiles together (U = 4 for W = 1,
+    2; 2 for W = 3, 4) once a workgroup owns at least U tiles, i.e. once the
+    shard has more tiles than U times that grid;
   * the update kernels switch from one workgroup per tile to a persistent grid
     with one contiguous part of the tiles per XCD past 8192 tiles (2^24
     elements);
@@ -33,6 +34,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.large]
 NORM_TOL = 1e-12
 TILE = 2048
 GRID = 2048            # the library's persistent grid: 8 workgroups per CU on 256 CUs
+FEW_GRID = 1536        # its sum-of-squares pass over 1-4 slices: 6 workgroups per CU
 
 
 @pytest.fixture(scope="module")
@@ -53,23 +55,24 @@ def slices(seed, t, W, S, begin, sigma):
     return [synth.bf16(S, synth.grad_key(seed, t, w), begin, sigma) for w in range(W)]
 
 
-# S per W: past U * 2048 tiles so every workgroup runs the U-tile loop body at
-# least once (W = 2: U = 4, here 8 tiles per workgroup, which also puts the
-# update past 8192 tiles; W = 3, 4: U = 2, more than 4 tiles per workgroup),
-# each with a ragged last tile
-RECOMPUTE_SHARDS = {2: (1 << 25) + 1001, 3: (1 << 24) + 4099, 4: (1 << 24) + 2053}
+# S per W: past U * 1536 tiles so every workgroup runs the U-tile loop body at
+# least once (W = 1, 2: U = 4, here more than 10 tiles per workgroup, which
+# also puts the update past 8192 tiles; W = 3, 4: U = 2, more than 5 tiles per
+# workgroup), each with a ragged last tile
+RECOMPUTE_SHARDS = {1: (1 << 25) + 777, 2: (1 << 25) + 1001, 3: (1 << 24) + 4099, 4: (1 << 24) + 2053}
 
 
-@pytest.mark.parametrize("W", [2, 3, 4])
+@pytest.mark.parametrize("W", [1, 2, 3, 4])
 def test_recompute_design_multi_tile_norm_pass(env, W):
     """zero1_mta_step with the default design for W <= 4 (recompute g in the
-    update), one flat tensor, 2 steps, rank 1 of W: full state bit for bit."""
+    update), one flat tensor, 2 steps, rank 1 of W (rank 0 at W = 1): full
+    state bit for bit."""
     torch, dev = env
     S = RECOMPUTE_SHARDS[W]
-    rank = 1
+    rank = min(1, W - 1)
     begin = rank * S
     seed = 0x1A26E0 + W
-    assert S // TILE > (8 // (4 if W == 3 else W)) * GRID
+    assert S // TILE > (4 if W <= 2 else 2) * FEW_GRID
     master0 = synth.f32(S, synth.master_key(seed), begin, 0.02)
     master = torch.from_numpy(master0.copy()).to(dev)
     m = torch.zeros(S, dtype=torch.float32, device=dev)

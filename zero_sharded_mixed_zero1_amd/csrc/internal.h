@@ -22,6 +22,9 @@ constexpr int kChunkElems = 2048;   // multi-tensor chunk: one tile
 #ifndef Z1_REDUCE_PER_CU
 #define Z1_REDUCE_PER_CU 8          // reduce: persistent grid of 8 workgroups per CU
 #endif
+#ifndef Z1_FEW_PER_CU
+#define Z1_FEW_PER_CU 6             // sum-of-squares pass over 1-4 slices: 6 workgroups per CU
+#endif
 #ifndef Z1_UPDATE_PER_CU
 #define Z1_UPDATE_PER_CU 8          // update past kMaxPartials units: 8 workgroups per CU
 #endif
@@ -35,6 +38,7 @@ constexpr size_t kPartialBytes = sizeof(double) * kMaxPartials;
 constexpr size_t kGOffset = kInfoBytes + kPartialBytes;   // multiple of 256
 
 constexpr int kReducePerCu = Z1_REDUCE_PER_CU;
+constexpr int kFewPerCu = Z1_FEW_PER_CU;
 constexpr int kUpdatePerCu = Z1_UPDATE_PER_CU;
 constexpr long long kGNtBytes = Z1_G_NT_BYTES;
 
@@ -112,6 +116,10 @@ void set_launch_events(hipEvent_t start, hipEvent_t stop);
 // non-temporal hint.
 hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out,
                          double* partials, int nblocks, int split, bool g_nt, hipStream_t s);
+// launch_reduce runs the few-slice sum-of-squares kernel (loads of several
+// tiles issued together, its own grid of kFewPerCu workgroups per CU) when it
+// only sums squares on the vector path over at most four slices.
+inline bool few_slice_pass(bool vec, bool store_g, bool norm, int W) { return vec && norm && !store_g && W <= 4; }
 // Sum of squares of an fp32 vector, one partial per workgroup.
 hipError_t launch_sumsq(const float* g, int64_t len, bool vec, double* partials,
                         int nblocks, int split, hipStream_t s);

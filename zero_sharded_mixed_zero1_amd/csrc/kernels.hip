@@ -328,8 +328,10 @@ __device__ __forceinline__ double block_sum(double x)
 // The sum-of-squares pass that stores nothing (the first pass of the
 // recompute design) over whole tiles when there are few slices: one tile of
 // WS slices is only 8*WS bytes per lane, too little in flight to keep HBM
-// busy, so the loads of U tiles (U*WS <= 8 slice words per lane) are issued
-// together.  The tiles are then reduced and squared in tile order, so acc
+// busy, so the loads of U tiles are issued together (U = 4 for one or two
+// slices, 2 for three or four; with the grid of kFewPerCu workgroups per CU,
+// the shape measured best on MI355X).  The tiles are then reduced and
+// squared in tile order, so acc
 // takes the same sequence of values as one tile at a time.  Returns the
 // first tile not processed.
 template <int WS, int U>
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Reduce r, int64_t len,
     int64_t t = u.lo;
     const int64_t full_end = VEC ? (u.hi < len / kTile ? u.hi : len / kTile) : u.lo;
     static_assert(FEW == 0 || (VEC && !STORE && NORM && FEW <= 4), "few-slice pass: vector, sum of squares only");
-    if constexpr (FEW > 0) t = norm_tiles<FEW, 8 / (FEW == 3 ? 4 : FEW)>(r, t, full_end, u.step, acc);
+    if constexpr (FEW > 0) t = norm_tiles<FEW, FEW <= 2 ? 4 : 2>(r, t, full_end, u.step, acc);
     if (VEC && t < full_end) {
         float sp[8];                // the previous tile's g, stored after the next tile's loads
         int64_t tp = t;
@@ -744,7 +746,7 @@ hipError_t launch_reduce(const Reduce& r, int64_t len, bool vec, float* g_out, d
     const dim3 grid(nblocks);
     const bool store = g_out != nullptr, norm = partials != nullptr;
     hipError_t e;
-    if (vec && norm && !store && r.W <= 4) {
+    if (few_slice_pass(vec, store, norm, r.W)) {
         switch (r.W) {
         case 1: return run(reduce_kernel<true, false, true, false, 1>, grid, s, r, len, g_out, partials, split);
         case 2: return run(reduce_kernel<true, false, true, false, 2>, grid, s, r, len, g_out, partials, split);
