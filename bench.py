@@ -271,8 +271,8 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
             cp.ws = torch.empty(z.mta_workspace_bytes(cp.plan, W, design_flags), dtype=torch.uint8, device=dev)
         cp.rsd = torch.zeros(W, dtype=torch.float64, device=dev)
         copies.append(cp)
+    spans = sorted(spans) if arena is not None else []
     if arena is not None:   # no two arrays of any copy overlap (checked before any step runs)
-        spans.sort()
         for (a0, b0), (a1, b1) in zip(spans, spans[1:]):
             if b0 > a1:
                 raise SystemExit(f"arena: arrays overlap at byte {a1}")
@@ -288,7 +288,8 @@ def setup(torch, cfg, design_flags, n_copies, dev, layout="arena"):
         for cp in copies[1:]:
             cp.rsd.copy_(c0.rsd)
     torch.cuda.synchronize()
-    return dict(W=W, rank=rank, N=N, S=S, begin=begin, pieces=len(pieces_l), copies=copies, info=info)
+    return dict(W=W, rank=rank, N=N, S=S, begin=begin, pieces=len(pieces_l), copies=copies, info=info,
+                arena=arena, spans=spans)
 
 
 # ---------------------------------------------------------------------- the step
@@ -459,6 +460,10 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
         gc.disable()
         res["graph"] = graph_timing(torch, z, cfg, st, design, warmup + 2 * steps + 100)
         gc.enable()
+    gc.collect()
+    gc.disable()
+    res["other_tensors"] = other_tensors(torch, z, cfg, st, design, warmup + 2 * steps + 300, steps, red_ms, upd_ms)
+    gc.enable()
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     cal = calibrated(torch, z, cfg, st, store_g, cus)
     if cal:
@@ -474,6 +479,68 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def arena_gaps(st, min_bytes=64 << 20):
+    """[a, b) byte ranges of the arena that no array of the step occupies
+    (the gaps between the spaced arrays), at least min_bytes each."""
+    total, pos, gaps = st["arena"].numel(), 0, []
+    for a, b in st["spans"]:
+        if a - pos >= min_bytes:
+            gaps.append((pos, a))
+        pos = max(pos, b)
+    if total - pos >= min_bytes:
+        gaps.append((pos, total))
+    return gaps
+
+
+OTHER_BYTES_PER_STEP = 4 << 30   # other tensors' writes between two steps
+
+
+def other_tensors(torch, z, cfg, st, design, k0, steps, idle_red_ms, idle_upd_ms):
+    """The step inside a training process whose other tensors are written
+    between two optimizer steps: 4 GiB of writes (1 GiB fills) before each
+    step -- in the arena layout into its gaps, every gap byte written once
+    first (the gaps hold the other tensors); with one allocation per array into
+    one separate 1 GiB tensor -- and the step's two kernels timed by their own
+    dispatches, as in the idle passes."""
+    dev = st["copies"][0].master.device
+    if st["arena"] is not None:
+        gaps = arena_gaps(st)
+        if not gaps:
+            return None
+        views = [st["arena"][a:b] for a, b in gaps]
+        for v in views:
+            v.fill_(0x5A)
+        where = f"the arena's {len(gaps)} gaps ({sum(b - a for a, b in gaps)} B, every byte written once first)"
+    else:
+        views = [torch.empty(1 << 30, dtype=torch.uint8, device=dev)]
+        where = "one separate 1 GiB tensor"
+    torch.cuda.synchronize()
+
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    events = [((event(), event()), (event(), event())) for _ in range(steps)]
+    fills = OTHER_BYTES_PER_STEP // (1 << 30)
+    written = 0
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for j in range(fills):
+            v = views[(i * fills + j) % len(views)]
+            n = min(1 << 30, v.numel())
+            o = ((i * fills + j) * n) % (v.numel() - n + 1)
+            v[o:o + n].fill_((i + j) & 0xFF)
+            written += n
+        run_steps(z, cfg, st, design, k0 + i, k0 + i + 1, [events[i]])
+    torch.cuda.synchronize()
+    red = statistics.fmean(e[0][0].elapsed_time(e[0][1]) for e in events)
+    upd = statistics.fmean(e[1][0].elapsed_time(e[1][1]) for e in events)
+    del views
+    return {"where": where, "written_per_step_bytes": written // steps, "reduce_ms": red, "update_ms": upd,
+            "kernels_ms": red + upd, "over_idle": (red + upd) / (idle_red_ms + idle_upd_ms)}
 
 
 # ---------------------------------------------------------------------- CPU baseline
@@ -992,7 +1059,8 @@ def main():
                      "calibrated_over_kernel": upd.get("calibrated_over_kernel")},
         "kernels": h["kernels"],
         "calibrated_ms_per_step": h.get("calibrated_ms_per_step"),
-        "layouts": {lay: {k: head[lay][k] for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout")}
+        "layouts": {lay: {k: head[lay][k]
+                          for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout", "other_tensors")}
                     for lay in layouts},
     }
     for extra in ("bucketed", "graph"):

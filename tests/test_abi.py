@@ -330,7 +330,8 @@ def test_bench_entry_points_and_gpu_count_contract():
     import sys
     import bench
     for name in ("setup", "run_steps", "measure", "calibrated", "calibrate", "cpu_baseline", "bucketed_timing",
-                 "summarize_pmc", "summarize_kt", "traffic_from_summary", "kernel_source_hash", "main"):
+                 "summarize_pmc", "summarize_kt", "traffic_from_summary", "kernel_source_hash", "other_tensors",
+                 "main"):
         assert callable(getattr(bench, name)), name
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
@@ -384,3 +385,25 @@ def test_profile_summaries_from_counter_and_trace_files(tmp_path):
     assert len(lines) == 2
     cols = [[c.strip() for c in l.split("|")] for l in lines]
     assert cols[0][1:4] == ["2048", "2", "51.00"] and cols[1][1:4] == ["768", "1", "9.00"]
+
+
+def test_bench_arena_gaps():
+    """The bench's gap finder returns exactly the byte ranges of the arena that
+    no array occupies (overlapping and touching spans merged, small gaps and
+    the space before, between and after the arrays handled alike)."""
+    import bench
+
+    class Arena:
+        def __init__(self, n):
+            self.n = n
+
+        def numel(self):
+            return self.n
+
+    st = {"arena": Arena(1000), "spans": [(0, 100), (50, 120), (120, 300), (305, 400), (700, 900)]}
+    assert bench.arena_gaps(st, min_bytes=1) == [(300, 305), (400, 700), (900, 1000)]
+    assert bench.arena_gaps(st, min_bytes=10) == [(400, 700), (900, 1000)]
+    st = {"arena": Arena(500), "spans": [(100, 200)]}
+    assert bench.arena_gaps(st, min_bytes=1) == [(0, 100), (200, 500)]
+    st = {"arena": Arena(200), "spans": [(0, 200)]}
+    assert bench.arena_gaps(st, min_bytes=1) == []
