@@ -415,8 +415,9 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
     run_steps(z, cfg, st, design, warmup + steps, warmup + 2 * steps, events)
     torch.cuda.synchronize()
     gc.enable()
-    upd_ms = statistics.fmean(e[1][0].elapsed_time(e[1][1]) for e in events)
-    red_ms = statistics.fmean(e[0][0].elapsed_time(e[0][1]) for e in events)
+    upd_t = [e[1][0].elapsed_time(e[1][1]) for e in events]
+    red_t = [e[0][0].elapsed_time(e[0][1]) for e in events]
+    upd_ms, red_ms = statistics.fmean(upd_t), statistics.fmean(red_t)
     ms = el * 1e3 / steps
     bpp = cfg.bytes_per_param
     fixed = 18 if cfg.mv_bf16 else 26
@@ -445,8 +446,9 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
                        "moved_GBps": upd_mv / (upd_ms * 1e-3) / 1e9},
         },
     }
-    for k in ("reduce", "update"):
+    for k, t in (("reduce", red_t), ("update", upd_t)):
         kk = res["kernels"][k]
+        kk["ms_median"], kk["ms_min"] = statistics.median(t), min(t)
         kk["frac_of_peak"] = kk["algorithmic_GBps"] / PEAK_HBM_GBS
         kk["traffic"] = traffic_from_summary(pmc_summary_path(cfg.name), k) if layout == "arena" else None
     if bucketed and store_g:
@@ -459,6 +461,18 @@ def measure(torch, z, cfg, layout, steps, warmup, dev, bucketed=False):
         gc.collect()
         gc.disable()
         res["graph"] = graph_timing(torch, z, cfg, st, design, warmup + 2 * steps + 100)
+        gc.enable()
+    if n_copies > 1:
+        # secondary figure: the same K steps on copy 0 alone, so that each step
+        # finds what the previous one left in the MALL
+        gc.collect()
+        gc.disable()
+        warm = dict(st, copies=st["copies"][:1])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(z, cfg, warm, design, warmup + 2 * steps, warmup + 3 * steps)
+        torch.cuda.synchronize()
+        res["mall_warm_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
         gc.enable()
     gc.collect()
     gc.disable()
@@ -1060,7 +1074,8 @@ def main():
         "kernels": h["kernels"],
         "calibrated_ms_per_step": h.get("calibrated_ms_per_step"),
         "layouts": {lay: {k: head[lay][k]
-                          for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout", "other_tensors")}
+                          for k in ("ms_per_step", "params_per_s", "pct_of_peak_hbm", "layout", "other_tensors",
+                                    "mall_warm_ms_per_step") if k in head[lay]}
                     for lay in layouts},
     }
     for extra in ("bucketed", "graph"):
