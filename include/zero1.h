@@ -404,9 +404,10 @@ zero1_status zero1_time_next_launch(void* start_event, void* stop_event);
  * --, master, m, v and the shard's bf16 parameters) move 5.7-5.8 TB/s when
  * they are 24 GiB or more apart and 4.5-5.0 TB/s when they are 12 GiB or
  * less apart (1 GiB streams, a kernel that only moves them); on the step, the
- * Llama-7B/8 shard's update moves 6.2 TB/s in the arena against 5.3 TB/s with
- * one allocation per array, and the whole 7e9-parameter W=1 step takes
- * 34.0 ms against 39.7.  The planner puts those five at one spacing D
+ * Llama-7B/8 shard's update moves 6.1-6.2 TB/s in the arena against 5.0-6.0
+ * TB/s with one allocation per array (that placement varies between
+ * processes), and the whole 7e9-parameter W=1 step takes 33.7-33.8 ms
+ * against 39.5-39.9.  The planner puts those five at one spacing D
  * (40 GiB, or more when an array is larger, or less when `capacity` is short)
  * and packs the remaining gradient buffers after the parameter buffer.  The
  * gaps between the spaced arrays are not used by the library: the caller may
