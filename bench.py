@@ -106,6 +106,8 @@ def cal_lib():
         P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L.zcal_stream.argtypes = [P, P, P, i32, P, P, P, i32, i64, i32, i32, i32, i32, i32, P, P]
         L.zcal_stream.restype = i32
+        L.zcal_policy_mix.argtypes = [i32, i32, P, P, P, P, P, i64, i32, i32, P]
+        L.zcal_policy_mix.restype = i32
         _cal = L
     return _cal
 
@@ -126,6 +128,14 @@ def zcal_stream(rd, wr, n_tiles, grid, split, sink, stream, tiles_in_flight=1, w
                                n_tiles, tiles_in_flight, wide, contig, grid, split, sink, stream)
     if st != 0:
         raise RuntimeError(f"zcal_stream failed with status {st}")
+
+
+def zcal_policy_mix(rd_policy, wr_policy, g, p, m, v, out, n_tiles, grid, split, stream):
+    """One pass of the update's stream mix with explicit cache-policy bits
+    (1 sc0, 2 nt, 16 sc1) on its loads and stores."""
+    st = cal_lib().zcal_policy_mix(rd_policy, wr_policy, g, p, m, v, out, n_tiles, grid, split, stream)
+    if st != 0:
+        raise RuntimeError(f"zcal_policy_mix failed with status {st}")
 
 
 def best_calibration(torch, rd, wr, n_tiles, grid, split, sink, stream, reps=5):
@@ -945,7 +955,39 @@ def calibrate(torch, dev, gib=4, spacing_gib=40):
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
     out["update_mix_by_spacing_GBps"] = spacing_sweep(torch, dev, sink, stream, cus)
+    out["update_mix_by_cache_policy_GBps"] = policy_sweep(torch, dev, stream, cus)
     return out
+
+
+POLICY_NAMES = {0: "none", 1: "sc0", 2: "nt", 3: "sc0 nt", 16: "sc1", 17: "sc0 sc1", 18: "nt sc1",
+                19: "sc0 nt sc1"}
+
+
+def policy_sweep(torch, dev, stream, cus, spacing_gib=40):
+    """The recompute design's update mix at W = 1 (a bf16 gradient read;
+    master, m, v read and rewritten; bf16 parameters written: 28 bytes per
+    element) over 1 GiB fp32 streams spacing_gib GiB apart, for each pair of
+    cache policies on its loads and its stores: {"load / store": GB/s}."""
+    n = (1 << 30) // 4 // 2048 * 2048
+    n_tiles = n // 2048
+    D = spacing_gib << 30
+    arena = torch.empty(4 * D + 2 * n, dtype=torch.uint8, device=dev)
+    arena.fill_(0x3c)
+    g, p, m, v, o = (arena.data_ptr() + k * D for k in range(5))
+    res = {}
+    for rp in (2, 0, 16, 18):
+        for wp in (2, 0, 1, 16, 17, 18):
+            fn = lambda: zcal_policy_mix(rp, wp, g, p, m, v, o, n_tiles, 8 * cus, 8, stream)  # noqa: E731
+            fn()
+            torch.cuda.synchronize()
+            ms = timed_passes(torch, fn, 5)
+            key = f"{POLICY_NAMES[rp]} / {POLICY_NAMES[wp]}"
+            res[key] = n_tiles * 2048 * 28 / (ms * 1e-3) / 1e9
+            log(f"calibrate update mix, loads {POLICY_NAMES[rp]}, stores {POLICY_NAMES[wp]}: {res[key]:.0f} GB/s")
+    del arena
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def spacing_sweep(torch, dev, sink, stream, cus, spacings_gib=(1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48)):

@@ -67,3 +67,39 @@ def test_two_read_streams_arrive_as_their_xor(env):
     run(torch, dev, [(ta.data_ptr(), 4, False), (tb.data_ptr(), 4, True)], [(out.data_ptr(), 4, False)],
         n_tiles, 64, 8, 2, 0, 1)
     assert np.array_equal(out.cpu().numpy(), a ^ b)
+
+
+@pytest.mark.parametrize("rp,wp", [(2, 2), (0, 17), (18, 16), (16, 1)])
+def test_policy_mix_moves_every_stream_exactly(env, rp, wp):
+    """zcal_policy_mix (the update's stream mix with explicit cache-policy
+    bits) reads every element of g, p, m, v and writes every element of p, m,
+    v and out exactly once: per lane and tile, s = the xor of its four g words,
+    p, m, v ^= s, out words = s; nothing outside the covered range changes."""
+    torch, dev = env
+    rng = np.random.default_rng(rp * 100 + wp)
+    lane = np.arange(256)
+    a = 512 * (lane >> 6) + 4 * (lane & 63)
+    for n_tiles, grid, split in ((37, 16, 8), (3001, 2048, 8), (5, 2048, 1)):
+        n = n_tiles * 2048
+        host = {k: rng.integers(0, 2**32, size=(n + 2 * GUARD) // (2 if k in "go" else 1),
+                                dtype=np.uint64).astype(np.uint32) for k in "gpmvo"}
+        dev_t = {k: torch.from_numpy(host[k].view(np.int32).copy()).to(dev) for k in host}
+        ptr = {k: dev_t[k].data_ptr() + (2 if k in "go" else 4) * GUARD for k in host}
+        bench.zcal_policy_mix(rp, wp, ptr["g"], ptr["p"], ptr["m"], ptr["v"], ptr["o"], n_tiles, grid, split,
+                              torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        E = (np.arange(n_tiles)[:, None] * 2048 + a[None, :]).ravel()        # element index of quad 0
+        g32 = host["g"][GUARD // 2:GUARD // 2 + n // 2]
+        s = g32[E // 2] ^ g32[E // 2 + 1] ^ g32[(E + 256) // 2] ^ g32[(E + 256) // 2 + 1]
+        what = f"rp={rp} wp={wp} tiles={n_tiles} grid={grid} split={split}"
+        for k in "pmv":
+            exp = host[k].copy()
+            for off in (0, 1, 2, 3, 256, 257, 258, 259):
+                exp[GUARD + E + off] ^= s
+            got = dev_t[k].cpu().numpy().view(np.uint32)
+            assert np.array_equal(got, exp), k + " " + what
+        exp = host["o"].copy()
+        for w in (E // 2, E // 2 + 1, (E + 256) // 2, (E + 256) // 2 + 1):
+            exp[GUARD // 2 + w] = s
+        assert np.array_equal(dev_t["o"].cpu().numpy().view(np.uint32), exp), "out " + what
+        assert np.array_equal(dev_t["g"].cpu().numpy().view(np.uint32), host["g"]), "g changed " + what

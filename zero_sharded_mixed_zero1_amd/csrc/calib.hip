@@ -28,6 +28,9 @@
 // Every read stream is folded into a per-lane XOR (so no load can be dropped)
 // and every write stream receives that XOR, so the bytes moved are exactly
 // tiles * 2048 * (sum of the streams' element sizes).
+//
+// A second kernel (zcal_policy_mix) moves the update's own mix with explicit
+// cache-policy bits on its loads and stores, to measure what those bits do.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -180,9 +183,108 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Streams s, int64_t nti
         sink[blockIdx.x] = tot.w;
 }
 
+// The update's stream mix with explicit cache-policy bits: g (bf16) read;
+// p, m, v (fp32) read and rewritten in place; out (bf16) written.  RP and WP
+// are the policy operands of every buffer load and store (gfx950: 1 sc0,
+// 2 nt, 16 sc1, or-ed).  Per lane and tile: s = the xor of its four g words,
+// then p, m and v ^= s and every out word = s.
+template <int RP, int WP>
+__global__ __launch_bounds__(kThreads) void policy_mix_kernel(const uint16_t* g, uint32_t* p, uint32_t* m,
+                                                              uint32_t* v, uint16_t* out, int64_t ntiles,
+                                                              int split)
+{
+    const int64_t G = gridDim.x, b = blockIdx.x;
+    const int64_t nx = (split > 1 && G % split == 0) ? split : 1;
+    const int64_t x = b % nx, per = (ntiles + nx - 1) / nx;
+    const int64_t lo = x * per, hi = lo + per < ntiles ? lo + per : ntiles;
+    const int a = quad_a();
+    for (int64_t t = lo + b / nx; t < hi; t += G / nx) {
+        const int64_t e = t * kTile;
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g + e), 0,
+                                                                            kTile * 2, kBufDword3);
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(p + e, 0, kTile * 4, kBufDword3);
+        const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(m + e, 0, kTile * 4, kBufDword3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(v + e, 0, kTile * 4, kBufDword3);
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out + e, 0, kTile * 2, kBufDword3);
+        const u32x2 g0 = __builtin_amdgcn_raw_buffer_load_b64(rg, a * 2, 0, RP);
+        const u32x2 g1 = __builtin_amdgcn_raw_buffer_load_b64(rg, (a + 256) * 2, 0, RP);
+        const u32x4 p0 = __builtin_amdgcn_raw_buffer_load_b128(rp, a * 4, 0, RP);
+        const u32x4 p1 = __builtin_amdgcn_raw_buffer_load_b128(rp, (a + 256) * 4, 0, RP);
+        const u32x4 m0 = __builtin_amdgcn_raw_buffer_load_b128(rm, a * 4, 0, RP);
+        const u32x4 m1 = __builtin_amdgcn_raw_buffer_load_b128(rm, (a + 256) * 4, 0, RP);
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rv, a * 4, 0, RP);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rv, (a + 256) * 4, 0, RP);
+        const uint32_t sx = g0.x ^ g0.y ^ g1.x ^ g1.y;
+        __builtin_amdgcn_raw_buffer_store_b128(p0 ^ sx, rp, a * 4, 0, WP);
+        __builtin_amdgcn_raw_buffer_store_b128(p1 ^ sx, rp, (a + 256) * 4, 0, WP);
+        __builtin_amdgcn_raw_buffer_store_b128(m0 ^ sx, rm, a * 4, 0, WP);
+        __builtin_amdgcn_raw_buffer_store_b128(m1 ^ sx, rm, (a + 256) * 4, 0, WP);
+        __builtin_amdgcn_raw_buffer_store_b128(v0 ^ sx, rv, a * 4, 0, WP);
+        __builtin_amdgcn_raw_buffer_store_b128(v1 ^ sx, rv, (a + 256) * 4, 0, WP);
+        const u32x2 o = {sx, sx};
+        __builtin_amdgcn_raw_buffer_store_b64(o, ro, a * 2, 0, WP);
+        __builtin_amdgcn_raw_buffer_store_b64(o, ro, (a + 256) * 2, 0, WP);
+    }
+}
+
+typedef void (*PolicyKernel)(const uint16_t*, uint32_t*, uint32_t*, uint32_t*, uint16_t*, int64_t, int);
+
+template <int RP>
+PolicyKernel policy_kernel_w(int wp)
+{
+    switch (wp) {
+    case 0: return policy_mix_kernel<RP, 0>;
+    case 1: return policy_mix_kernel<RP, 1>;
+    case 2: return policy_mix_kernel<RP, 2>;
+    case 3: return policy_mix_kernel<RP, 3>;
+    case 16: return policy_mix_kernel<RP, 16>;
+    case 17: return policy_mix_kernel<RP, 17>;
+    case 18: return policy_mix_kernel<RP, 18>;
+    case 19: return policy_mix_kernel<RP, 19>;
+    default: return nullptr;
+    }
+}
+
+PolicyKernel policy_kernel(int rp, int wp)
+{
+    switch (rp) {
+    case 0: return policy_kernel_w<0>(wp);
+    case 1: return policy_kernel_w<1>(wp);
+    case 2: return policy_kernel_w<2>(wp);
+    case 3: return policy_kernel_w<3>(wp);
+    case 16: return policy_kernel_w<16>(wp);
+    case 17: return policy_kernel_w<17>(wp);
+    case 18: return policy_kernel_w<18>(wp);
+    case 19: return policy_kernel_w<19>(wp);
+    default: return nullptr;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// The update's stream mix (policy_mix_kernel) over n_tiles * 2048 elements of
+// each stream, with cache-policy bits rd_policy on every load and wr_policy on
+// every store: each of 0, 1 (sc0), 2 (nt), 3, 16 (sc1), 17, 18, 19.  g and out
+// hold bf16 elements, p, m and v 4-byte ones; all 16-byte aligned and pairwise
+// disjoint.  grid, split as for zcal_stream.  Returns 0, 1 for a bad argument,
+// or 2 + the HIP error code of the launch.
+int zcal_policy_mix(int rd_policy, int wr_policy, const void* g, void* p, void* m, void* v, void* out,
+                    int64_t n_tiles, int grid, int split, void* stream)
+{
+    const PolicyKernel k = policy_kernel(rd_policy, wr_policy);
+    const void* ptrs[5] = {g, p, m, v, out};
+    if (!k || n_tiles < 0 || grid < 1 || (split != 1 && split != 8)) return 1;
+    for (const void* q : ptrs)
+        if (!q || reinterpret_cast<uintptr_t>(q) % 16) return 1;
+    if (n_tiles == 0) return 0;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint16_t*>(g), static_cast<uint32_t*>(p), static_cast<uint32_t*>(m),
+                       static_cast<uint32_t*>(v), static_cast<uint16_t*>(out), n_tiles, split);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : 2 + (int)e;
+}
 
 // One pass over n_tiles * 2048 elements of every stream.
 //   rd[n_rd]: read streams (device pointers, 16-byte aligned); rd_bytes: their
