@@ -1,7 +1,9 @@
 """bench.py end to end on the small workload (flat 2^20 parameters, W=4): it
 prints one JSON line with the metric, the throughput, the roofline object of
 the dominant kernel and the CPU baseline, and the figures agree with each
-other (params/s from ms/step, the roofline fraction from its own fields)."""
+other (params/s from ms/step, the roofline fraction from its own fields); the
+secondary measurements (kernel median and minimum, other tensors written
+between steps, the MALL-warm step) are present in both layouts."""
 from __future__ import annotations
 
 import json
@@ -40,3 +42,12 @@ def test_bench_line_contract():
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["single_thread"]["cores"] == 1
     assert set(d["layouts"]) == {"arena", "packed"} and "graph" in d
+    for k in ("reduce", "update"):   # each kernel's mean, median and minimum of its K durations
+        kk = d["kernels"][k]
+        assert 0 < kk["ms_min"] <= kk["ms_median"] and kk["ms_min"] <= kk["ms"], (k, kk)
+    for lay in ("arena", "packed"):
+        e = d["layouts"][lay]
+        o = e["other_tensors"]   # the step's kernels with 4 GiB of other writes before each step
+        assert o["written_per_step_bytes"] == 4 << 30 and o["kernels_ms"] > 0, (lay, o)
+        assert ("gaps" in o["where"]) == (lay == "arena"), o["where"]
+        assert e["mall_warm_ms_per_step"] > 0   # the rotated workload's steps on one copy
