@@ -984,6 +984,31 @@ def test_random_configurations(env, case):
                       lambda t: scale * (1 + t), max_norm=max_norm, ranks=[r], variant=variant)
 
 
+@pytest.mark.parametrize("case", range(60))
+def test_random_configurations_wide(env, case):
+    """Seeded random configurations over the whole replica range (W up to
+    128) with larger tensors (up to 300,000 elements each, any alignment):
+    design, moment storage, state layout, compatibility variant and clip
+    threshold drawn at random, two steps, one random rank, bit-exact against
+    the oracle."""
+    torch, dev = env
+    rng = np.random.default_rng(0xF022 + case)
+    W = int(rng.integers(1, 129))
+    sizes = [int(rng.integers(1, 300001)) for _ in range(int(rng.integers(1, 12)))]
+    design = int(rng.choice([z.STORE_G, z.RECOMPUTE_G]))
+    mv_bf16 = bool(rng.integers(0, 2))
+    flat_state = bool(rng.integers(0, 2))
+    variant = int(rng.choice([0, 0, oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16]))
+    max_norm = float(rng.choice([1.0, 0.05, math.inf]))
+    scale = float(rng.choice([1e-4, 1e-2, 0.3]))
+    r = int(rng.integers(0, W))
+    _, S = z.shard_range(sum(sizes), W, r)
+    if S == 0:
+        r = 0
+    run_mta_all_ranks(torch, dev, sizes, W, 2, 0xF100 + case, design, mv_bf16, flat_state,
+                      lambda t: scale * (1 + t), max_norm=max_norm, ranks=[r], variant=variant)
+
+
 # (sum only, compatibility variant) of each random-cut case
 BUCKET_VARIANTS = [(False, 0), (False, oracle.G_BF16 | oracle.DECAY_FIRST), (True, 0),
                    (True, oracle.CLIP_EPS | oracle.G_BF16)]
