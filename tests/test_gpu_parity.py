@@ -188,6 +188,82 @@ def test_adamw_step_flat_parity(env, mv_bf16, source):
         assert_bf16_equal(to_np_u16(gp), oparam, "param " + what)
 
 
+@pytest.mark.parametrize("case", range(30))
+def test_flat_entry_points_random(env, case):
+    """Seeded random calls of the flat entry points, two steps each:
+    zero1_shard_reduce (g and this rank's sum of squares) then
+    zero1_adamw_step with that g, or zero1_adamw_step recomputing g from the
+    slices (with zero1_shard_reduce giving the sum of squares alone); W from 1
+    to 128, lengths from 0 to 200,000 at any offset into the replica buffers,
+    state buffers on or off 16-byte boundaries, sum or average, fp32 or bf16
+    moments, compatibility variants, t up to 2000.  State bit for bit, the
+    partial to 1e-12, the clip decision and coefficient identical."""
+    torch, dev = env
+    rng = np.random.default_rng(0xF1A7 + case)
+    W = int(rng.integers(1, 129))
+    length = int(rng.choice([0, 1, 2047, 2048, int(rng.integers(1, 200001)), int(rng.integers(1, 200001))]))
+    offset = int(rng.integers(0, 9))
+    from_g = bool(rng.integers(0, 2))
+    mv_bf16 = bool(rng.integers(0, 2))
+    sum_only = bool(rng.integers(0, 4) == 0)
+    variant = int(rng.choice([0, 0, oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16,
+                              oracle.DECAY_FIRST | oracle.G_BF16]))
+    t0 = int(rng.integers(1, 2001))
+    max_norm = float(rng.choice([1.0, 0.05, math.inf]))
+    sigma = float(rng.choice([1e-4, 1e-2, 0.3]))
+    skew = int(rng.integers(0, 2))            # 1: state buffers one element past an aligned start
+    n_ranks = int(rng.integers(1, 5))        # this rank is rank 0
+    seed = 0xF1B0 + case
+    N = offset + length
+    master0 = synth.f32(N + 1, synth.master_key(seed), 0, 0.02)[offset:offset + length].copy()
+    mvd, npmv = (torch.int16, np.uint16) if mv_bf16 else (torch.float32, np.float32)
+
+    def buf(n, dt):
+        return torch.zeros(n + skew, dtype=dt, device=dev)[skew:]
+
+    gm, gmm, gvv, gp = buf(length, torch.float32), buf(length, mvd), buf(length, mvd), buf(length, torch.int16)
+    gm.copy_(torch.from_numpy(master0))
+    om, ov = np.zeros(length, npmv), np.zeros(length, npmv)
+    omaster, oparam = master0.copy(), np.zeros(length, np.uint16)
+    ws = ws_tensor(torch, z.workspace_bytes(length, W), dev)
+    gbuf = torch.empty(max(length, 1), dtype=torch.float32, device=dev)
+    info = torch.zeros(4, dtype=torch.float64, device=dev)
+    sq = torch.zeros(1, dtype=torch.float64, device=dev)
+    red_flags = (z.SUM_ONLY if sum_only else 0) | (z.G_BF16 if variant & oracle.G_BF16 else 0)
+    upd_flags = (z.MV_BF16 if mv_bf16 else 0) | lib_flags(variant & (oracle.DECAY_FIRST | oracle.CLIP_EPS))
+    what = (f"case={case} W={W} len={length} off={offset} from_g={from_g} bf16mv={mv_bf16} sum_only={sum_only} "
+            f"variant={variant} skew={skew} ranks={n_ranks} t0={t0}")
+    for t in (t0, t0 + 1):
+        G = replicas(seed, t, W, N + 1, sigma, outlier_pct=1, specials=3, rng=rng)   # one element past the range
+        hp = hp_at(t, max_norm=max_norm)
+        rs = np.concatenate([[0.0], rng.random(n_ranks - 1) * 3.0])
+        oinfo = oracle.step([g[offset:offset + length] for g in G], omaster, om, ov, oparam, hp, rs, 0,
+                            average=not sum_only, variant=variant)
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        z.shard_reduce(gd, offset, length, g_out=gbuf if from_g else None, sumsq_out=sq, flags=red_flags, ws=ws)
+        torch.cuda.synchronize()
+        assert rel_close(sq.item(), rs[0], NORM_TOL), (what, sq.item(), rs[0])
+        rsd = torch.from_numpy(rs).to(dev)                 # the oracle's partials: the norms agree bit for bit
+        if from_g:
+            z.adamw_step(gbuf, None, 0, length, gm, gmm, gvv, gp, hp, rsd, n_ranks, flags=upd_flags, info_out=info)
+        else:
+            z.adamw_step(None, gd, offset, length, gm, gmm, gvv, gp, hp, rsd, n_ranks, flags=upd_flags | red_flags,
+                         info_out=info)
+        torch.cuda.synchronize()
+        ni = info.cpu().numpy()
+        assert ni[1] == oinfo.norm or (math.isnan(ni[1]) and math.isnan(oinfo.norm)), what
+        assert bool(ni.view(np.int32)[5]) == oinfo.clip, what
+        assert ni[2:3].view(np.float32)[0] == oinfo.coef or oinfo.coef != oinfo.coef, what
+    assert_f32_equal(gm.cpu().numpy(), omaster, "master " + what)
+    if mv_bf16:
+        assert_bf16_equal(to_np_u16(gmm), om, "m " + what)
+        assert_bf16_equal(to_np_u16(gvv), ov, "v " + what)
+    else:
+        assert_f32_equal(gmm.cpu().numpy(), om, "m " + what)
+        assert_f32_equal(gvv.cpu().numpy(), ov, "v " + what)
+    assert_bf16_equal(to_np_u16(gp), oparam, "param " + what)
+
+
 # ---------------------------------------------------------------- multi-tensor apply
 RAGGED = [3000, 17, 5000, 8, 2203, 1, 65536 + 3, 768, 8192 * 2, 40000]
 # ragged against the 2048-element tiles but every piece 8-aligned, and a total
