@@ -1140,6 +1140,72 @@ def test_bucketed_reduction_random_cuts(env, case):
     assert_bf16_equal(p, o.param, "param")
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_bucketed_reduction_random_wide(env, case):
+    """The bucketed flow over random tensor lists and replica counts (W from 1
+    to 128), up to 40 buckets cut anywhere and reduced in a random order, sum
+    or average, fp32 or bf16 moments, flat or per-tensor state, compatibility
+    variants, two steps.  The bucket partials' sum matches the oracle's
+    partial to 1e-12; the update then gets the oracle's partials (so that the
+    norm is the same double) and the state equals the oracle's bit for bit."""
+    torch, dev = env
+    rng = np.random.default_rng(0xB1D0 + case)
+    W = int(rng.integers(1, 129))
+    numels = [int(rng.integers(1, 100001)) for _ in range(int(rng.integers(1, 12)))]
+    N = sum(numels)
+    sum_only = bool(rng.integers(0, 4) == 0)
+    variant = int(rng.choice([0, 0, oracle.DECAY_FIRST, oracle.CLIP_EPS, oracle.G_BF16]))
+    mv_bf16 = bool(rng.integers(0, 2))
+    flat_state = bool(rng.integers(0, 2))
+    flags = z.STORE_G | (z.SUM_ONLY if sum_only else 0) | lib_flags(variant)
+    rflags = flags & (z.STORE_G | z.SUM_ONLY | z.G_BF16)
+    r = int(rng.integers(0, W))
+    if z.shard_range(N, W, r)[1] == 0:
+        r = 0
+    seed = 0xE300 + case
+    master_full = synth.f32(N, synth.master_key(seed), 0, 0.02)
+    sh = MtaShard(torch, dev, numels, W, r, master_full, mv_bf16, flat_state)
+    ws = sh.workspace(z.STORE_G)
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[sh.begin:sh.begin + sh.S], mv_bf16)
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    what = f"case={case} W={W} numels={numels} rank={r} sum_only={sum_only} variant={variant} bf16mv={mv_bf16}"
+    for t in (1, 2):
+        n_cuts = int(rng.integers(0, 40))
+        cuts = np.unique(np.concatenate([[0, sh.S], rng.integers(0, sh.S + 1, size=n_cuts)]))
+        ranges = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:])]
+        parts = torch.zeros(max(len(ranges), 1), dtype=torch.float64, device=dev)
+        G = replicas(seed, t, W, N, float(rng.choice([1e-3, 0.3])), outlier_pct=1)
+
+        def reduced(q0, n):
+            gr = oracle.shard_reduce([g[q0:q0 + n] for g in G], average=not sum_only)
+            return oracle.round_to_bf16(gr) if variant & oracle.G_BF16 else gr
+
+        part = np.array([oracle.sumsq(reduced(q0, n)) for q0, n in (z.shard_range(N, W, q) for q in range(W))])
+        for k in rng.permutation(len(ranges)):
+            lo, hi = ranges[k]
+            bucket = [to_dev_u16(torch, g[sh.begin + lo:sh.begin + hi].copy(), dev) for g in G]
+            z.mta_reduce_range(bucket, sh.plan, lo, hi, parts[k:k + 1], flags=rflags, ws=ws)
+        z.partials_sum(parts, len(ranges), rsd[r:r + 1])
+        torch.cuda.synchronize()
+        assert rel_close(rsd[r].item(), part[r], NORM_TOL), (what, rsd[r].item(), part[r])
+        rsd.copy_(torch.from_numpy(part))
+        gd = [to_dev_u16(torch, g, dev) for g in G]
+        z.mta_update(gd, sh.begin, sh.plan, hp_at(t), rsd, W, flags=flags, ws=ws)
+        torch.cuda.synchronize()
+        oracle.step([g[sh.begin:sh.begin + sh.S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), part.copy(), r,
+                    average=not sum_only, variant=variant)
+    master, m, v, p = sh.gather()
+    assert_f32_equal(master, o.master, "master " + what)
+    if mv_bf16:
+        assert_bf16_equal(m, o.m, "m " + what)
+        assert_bf16_equal(v, o.v, "v " + what)
+    else:
+        assert_f32_equal(m, o.m, "m " + what)
+        assert_f32_equal(v, o.v, "v " + what)
+    assert_bf16_equal(p, o.param, "param " + what)
+
+
 def test_kernel_scoped_timing(env):
     """zero1_time_next_launch: a timed step gives bit for bit the state of an
     untimed one; each kernel's own duration is positive and the two together
