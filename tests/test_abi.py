@@ -407,3 +407,37 @@ def test_bench_arena_gaps():
     assert bench.arena_gaps(st, min_bytes=1) == [(0, 100), (200, 500)]
     st = {"arena": Arena(200), "spans": [(0, 200)]}
     assert bench.arena_gaps(st, min_bytes=1) == []
+
+
+def test_arena_tensors_views():
+    """arena_tensors (CPU memory here: the planner is host code) gives views of
+    the right type and length at the planner's offsets from a 2 MiB-aligned
+    base: the spaced arrays' shard starts on 2 MiB boundaries, no two arrays
+    overlapping, everything inside the one allocation."""
+    import torch
+    import zero_sharded_mixed_zero1_amd as z
+    S, W, N, b = 5000, 3, 15000, 5000
+    for flags in (z.STORE_G, z.RECOMPUTE_G | z.MV_BF16, 0):
+        a = z.arena_tensors(S, W, N, b, N, b, flags=flags, device="cpu", capacity=256 << 20)
+        L = a.layout
+        assert L.total_bytes <= 256 << 20 and a.storage.numel() == L.total_bytes + (2 << 20)
+        base = a.storage.data_ptr() + a.base
+        assert base % (2 << 20) == 0
+        mv = torch.int16 if flags & z.MV_BF16 else torch.float32
+        assert a.master.dtype == torch.float32 and a.master.numel() == S
+        assert a.m.dtype == mv and a.v.dtype == mv and a.m.numel() == S and a.v.numel() == S
+        assert a.params.dtype == torch.int16 and a.params.numel() == N
+        assert len(a.grads) == W and all(g.dtype == torch.int16 and g.numel() == N for g in a.grads)
+        assert a.ws.numel() == L.ws_bytes == z.mta_workspace_bytes(
+            z.Plan(shard_len=S), W, flags & (z.STORE_G | z.RECOMPUTE_G))
+        for t, off in ((a.master, L.master), (a.m, L.m), (a.v, L.v), (a.params, L.params), (a.ws, L.ws)):
+            assert t.data_ptr() == base + off
+        starts = [a.master.data_ptr(), a.m.data_ptr(), a.v.data_ptr(), a.params.data_ptr() + 2 * b]
+        starts.append(a.ws.data_ptr() if flags & z.STORE_G or (not flags & z.RECOMPUTE_G and W > 4)
+                      else a.grads[0].data_ptr() + 2 * b)
+        assert all(p % (2 << 20) == 0 for p in starts), [p % (2 << 20) for p in starts]
+        spans = sorted((t.data_ptr(), t.data_ptr() + t.numel() * t.element_size())
+                       for t in [a.ws, a.master, a.m, a.v, a.params] + a.grads)
+        assert all(e0 <= s1 for (_, e0), (s1, _) in zip(spans, spans[1:])), spans
+        lo, hi = a.storage.data_ptr(), a.storage.data_ptr() + a.storage.numel()
+        assert lo <= spans[0][0] and spans[-1][1] <= hi

@@ -766,6 +766,57 @@ def test_mta_step_in_planned_arena(env, design):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("W,mv_bf16", [(8, False), (3, True)])
+def test_arena_tensors_step(env, W, mv_bf16):
+    """The arena helper as a training loop would use it: z.arena_tensors for
+    the rank's arrays (full replica gradients, the whole parameter buffer),
+    the plan built over its views, two steps with the design the library
+    picks (store-g at W = 8, recompute at W = 3): bit-exact against the
+    oracle, and the parameters outside the shard untouched."""
+    torch, dev = env
+    numels = RAGGED
+    N, r = sum(numels), 1
+    begin, S = z.shard_range(N, W, r)
+    flags = z.MV_BF16 if mv_bf16 else 0
+    a = z.arena_tensors(S, W, N, begin, N, begin, flags=flags, device=dev)
+    master_full = synth.f32(N, synth.master_key(0xF400 + W), 0, 0.02)
+    a.master.copy_(torch.from_numpy(master_full[begin:begin + S].copy()))
+    a.m.zero_()
+    a.v.zero_()
+    a.params.zero_()
+    from tests.oracle_sim import RankState
+    o = RankState(master_full[begin:begin + S], mv_bf16)
+    offs = np.concatenate([[0], np.cumsum(numels)])
+    pieces = [(n, so, a.params[offs[ti] + off:], a.master[so:], a.m[so:], a.v[so:])
+              for ti, off, so, n in z.shard_pieces(numels, begin, begin + S)]
+    table = torch.empty(max(256, z.mta_table_bytes(pieces)), dtype=torch.uint8, device=dev)
+    plan = z.mta_plan(pieces, table, flags=flags)
+    assert z.mta_design(a.grads, begin, plan) == (z.STORE_G if W > 4 else z.RECOMPUTE_G)
+    rsd = torch.zeros(W, dtype=torch.float64, device=dev)
+    for t in (1, 2):
+        G = replicas(0xF400 + W, t, W, N, [0.02, 0.3][t - 1], outlier_pct=1)
+        for w in range(W):
+            a.grads[w].copy_(torch.from_numpy(G[w].view(np.int16)))
+        part = np.array([oracle.sumsq(oracle.shard_reduce([g[b:b + n] for g in G]))
+                         for b, n in (z.shard_range(N, W, q) for q in range(W))])
+        rsd.copy_(torch.from_numpy(part))
+        z.mta_step(a.grads, begin, plan, hp_at(t), rsd, W, r, ws=a.ws)
+        torch.cuda.synchronize()
+        oracle.step([g[begin:begin + S] for g in G], o.master, o.m, o.v, o.param, hp_at(t), part.copy(), r)
+    assert_f32_equal(a.master.cpu().numpy(), o.master, "master")
+    if mv_bf16:
+        assert_bf16_equal(to_np_u16(a.m), o.m, "m")
+        assert_bf16_equal(to_np_u16(a.v), o.v, "v")
+    else:
+        assert_f32_equal(a.m.cpu().numpy(), o.m, "m")
+        assert_f32_equal(a.v.cpu().numpy(), o.v, "v")
+    p_all = to_np_u16(a.params)
+    assert_bf16_equal(p_all[begin:begin + S], o.param, "params")
+    assert not p_all[:begin].any() and not p_all[begin + S:].any()
+    del a
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("design", [z.STORE_G, z.RECOMPUTE_G])
 def test_mta_step_captured_in_a_graph(env, design):
     """The step captured into a HIP graph (torch.cuda.graph) and replayed three

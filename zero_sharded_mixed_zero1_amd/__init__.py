@@ -16,3 +16,4 @@ from .binding import (  # noqa: F401
     lib, lib_path,
 )
 from .layout import shard_pieces  # noqa: F401
+from .arena import Arena, arena_tensors  # noqa: F401
