@@ -956,7 +956,48 @@ def calibrate(torch, dev, gib=4, spacing_gib=40):
             torch.cuda.empty_cache()
     out["update_mix_by_spacing_GBps"] = spacing_sweep(torch, dev, sink, stream, cus)
     out["update_mix_by_cache_policy_GBps"] = policy_sweep(torch, dev, stream, cus)
+    out["update_mix_random_placements"] = placement_search(torch, dev, stream, cus)
     return out
+
+
+def placement_search(torch, dev, stream, cus, n_placements=40, seed=7, span_gib=200, min_gap_gib=5):
+    """The W=1 update mix (zcal_policy_mix, nt loads and stores) over 1 GiB
+    fp32 streams placed at random whole-GiB offsets inside one span_gib GiB
+    allocation (each stream at least min_gap_gib GiB from the next), against
+    the planner's uniform 40 GiB spacing: {"uniform_40_GBps", "placements":
+    [[offsets in GiB of g, p, m, v, out], GB/s] ...}."""
+    import numpy as np
+    GiB = 1 << 30
+    n = GiB // 4 // 2048 * 2048
+    n_tiles = n // 2048
+    arena = torch.empty(span_gib * GiB, dtype=torch.uint8, device=dev)
+    arena.fill_(0x3c)
+    base = (arena.data_ptr() + (2 << 20) - 1) // (2 << 20) * (2 << 20)
+    assert base - arena.data_ptr() + (span_gib - 2) * GiB + 4 * n <= span_gib * GiB
+
+    def rate(offs):
+        ptr = [base + o * GiB for o in offs]
+        fn = lambda: zcal_policy_mix(2, 2, *ptr, n_tiles, 8 * cus, 8, stream)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        return n_tiles * 2048 * 28 / (timed_passes(torch, fn, 5) * 1e-3) / 1e9
+
+    rng = np.random.default_rng(seed)
+    res = {"uniform_40_GBps": rate([0, 40, 80, 120, 160]), "placements": []}
+    for _ in range(n_placements):
+        while True:
+            offs = sorted(int(x) for x in rng.choice(span_gib - 2, size=5, replace=False))
+            if all(b - a >= min_gap_gib for a, b in zip(offs, offs[1:])):
+                break
+        o = [offs[i] for i in rng.permutation(5)]
+        res["placements"].append([o, rate(o)])
+    rates = sorted(r for _, r in res["placements"])
+    log(f"calibrate update mix, {n_placements} random placements: min {rates[0]:.0f}, median "
+        f"{rates[len(rates) // 2]:.0f}, max {rates[-1]:.0f} GB/s; uniform 40 GiB {res['uniform_40_GBps']:.0f}")
+    del arena
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 POLICY_NAMES = {0: "none", 1: "sc0", 2: "nt", 3: "sc0 nt", 16: "sc1", 17: "sc0 sc1", 18: "nt sc1",
