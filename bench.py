@@ -24,7 +24,10 @@ Per kernel the line gives the algorithmic bytes over its own duration (HIP
 events stamped by the kernel's dispatch), the bytes the design moves, and a
 same-traffic calibration: the time of a kernel that moves exactly the same
 streams with the same access pattern and placement and computes nothing
-(libzero1_calib.so).
+(libzero1_calib.so).  Secondary passes in each layout: the step's kernels with
+4 GiB of other tensors written before every step (in the arena's gaps, or a
+separate tensor), and, for the workloads that rotate copies, the same steps on
+one copy (MALL-warm).
 
 Prints ONE JSON line.  Metric: shard parameters updated per second; the
 algorithmic HBM traffic is (2W+26) bytes per parameter (W bf16 gradient reads,
@@ -33,7 +36,9 @@ fp32 master/m/v read + write, bf16 parameter write; 2W+18 with bf16 m, v).
 Modes:
   python bench.py [--steps K] [--warmup W]                     the benchmark line
   python bench.py --config C4 [--layout arena] --no-per-config one workload only
-  python bench.py --calibrate                                  plain read/write/copy rates
+  python bench.py --calibrate                                  plain read/write/copy rates, the step's
+                                                               mixes, spacing, cache-policy and
+                                                               placement sweeps
   python bench.py --pmc-run --config C                         short run for rocprofv3 --pmc
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR OUT      counter summary for profiles/
   python bench.py --summarize-kt KT_DIR OUT                    kernel-trace summary for profiles/
