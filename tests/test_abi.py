@@ -3,7 +3,6 @@ every function include/zero1.h declares, and rejects bad arguments before it
 touches the device.  Also the host layout helpers."""
 from __future__ import annotations
 
-import ctypes
 import math
 import os
 import re

@@ -18,7 +18,6 @@ design), against the CPU oracle.
 """
 from __future__ import annotations
 
-import math
 import sys
 import time
 
@@ -29,7 +28,7 @@ import oracle
 import synth
 import zero_sharded_mixed_zero1_amd as z
 from synth.workloads import configs, shard_range
-from tests.gpu_util import assert_bf16_equal, assert_f32_equal, rel_close, to_np_u16, torch_cuda, ws_tensor
+from tests.gpu_util import assert_bf16_equal, assert_f32_equal, rel_close, torch_cuda, ws_tensor
 
 pytestmark = [pytest.mark.gpu, pytest.mark.large]
 
